@@ -1,0 +1,190 @@
+/*
+ * maskattn.h -- C ABI of the masked attention backward library for AMD MI355X (gfx950).
+ *
+ * Two masked forms of the FlashAttention-style attention backward pass:
+ *
+ *  (A) GQA attention with a learnable per-head sink logit and a sliding-window causal
+ *      mask, BHSD layout.  Defined on the page "[Example] Add GQA Sink Backward BHSD with
+ *      robustness improvements" (tilelang-ascend PR 1): "Files Added" (forward with
+ *      online softmax + sink + sliding window; backward producing dSinks) and the commit
+ *      message of the 4->2 kernel revision (Phase0 Delta = sum(O*dO), a KV loop of five
+ *      GEMMs with softmax and dS, Phase5 dSink; outputs O, Delta, dQ, dK, dV, dSinks).
+ *
+ *  (B) Block-sparse MHA driven by a uint8 block mask [B, N, ceil(Sq/bx), ceil(Skv/by)],
+ *      BNSD layout, D = 128.  Defined on the page "knowledge(triton) ... #174"
+ *      (cannbot-knowledge PR 174), BlockSparseAttentionGrad runbook: "task features"
+ *      (inputs dO, O and the softmax statistics; outputs dQ, dK, dV), "optimisation 1"
+ *      (the host only checks shapes, allocates and views; the mask transpose and the
+ *      selection tables are built on the device; no token-level dense mask), and the
+ *      precision recipe (p = exp(s - lse), ds = p * (dp - delta), a row with no selected
+ *      block gets zero).
+ *
+ * Mathematical contract (fp64 statement; the library computes it with fp16/bf16 MFMA
+ * operands and fp32 accumulation):
+ *   s_ij   = scale * q_i . k_j                    (scale multiplies q.k; natural log domain)
+ *   vis    (A) 0 <= i - j < window;  window >= S is plain causal
+ *          (B) block_mask[b, n, i / bx, j / by] != 0
+ *   lse_i  = log(exp(sink_h) + sum_{j vis} exp(s_ij))          (A; the sink is not scaled)
+ *          = log(sum_{j vis} exp(s_ij)), -inf for an empty row (B)
+ *   P_ij   = vis ? exp(s_ij - lse_i) : 0,   O_i = sum_j P_ij v_j
+ *   D_i    = dO_i . O_i
+ *   dS_ij  = P_ij (dO_i . v_j - D_i)
+ *   dQ_i   = scale sum_j dS_ij k_j
+ *   dK_j   = scale sum_{h in group(kvh)} sum_i dS_ij q_i
+ *   dV_j   = sum_{h in group(kvh)} sum_i P_ij dO_i
+ *   dsink_h = - sum_b sum_i exp(sink_h - lse_i) D_i            (A only)
+ * GQA groups are contiguous: query head h uses key/value head h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer.  Tensors are dense, row-major, in the
+ *     layouts given per argument, 16-byte aligned.  Outputs must not alias inputs.
+ *   - dtype selects the element type of q, k, v, o, dout, dq, dk, dv: MA_F16 (IEEE
+ *     half) or MA_BF16 (bfloat16).  lse, sink, dsink and the workspace are fp32.
+ *   - stream is a hipStream_t (NULL = the null stream).  Every call only enqueues work
+ *     on that stream and returns; there is no host synchronisation inside.
+ *   - The caller owns every buffer.  The library allocates no memory and keeps no state
+ *     between calls; concurrent calls on different streams with different buffers are safe.
+ *   - Validation reads only the scalar arguments and pointer values (never device data).
+ *     On any error nothing is enqueued and the status says why.
+ *   - Every element of every output is written, including exact zeros for rows that no
+ *     visible pair touches.
+ *   - Supported: D = 128 only; S >= 1 (any length, ragged tails allowed); window >= 1;
+ *     bx, by multiples of 16 in [16, 128].
+ */
+#ifndef MASKATTN_H
+#define MASKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MA_OK = 0,            /* enqueued */
+  MA_EINVAL = 1,        /* null/misaligned pointer, non-positive size, Hq % Hkv != 0, window < 1, ... */
+  MA_EUNSUPPORTED = 2,  /* D != 128, bx/by not a multiple of 16 or > 128, unknown dtype */
+  MA_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() query */
+  MA_ELAUNCH = 4        /* the HIP runtime reported an error while enqueueing */
+};
+
+/* Element types of the activation tensors. */
+enum { MA_F16 = 0, MA_BF16 = 1 };
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* maskattn_strerror(int status);
+
+/* ---------------------------------------------------------------------------------
+ * (A) attn_sink_fwd: forward pass with sink and sliding window (support call; it
+ * produces the O and lse the backward consumes).  Page 1, "Files Added" (online
+ * softmax with attention sink + sliding window mask) and the 4->2 revision (forward
+ * -> O, lse).
+ *   q     [B, Hq,  S, D]  dtype          k, v [B, Hkv, S, D] dtype
+ *   sink  [Hq]            fp32 logits (may be -inf: no sink)
+ *   o     [B, Hq,  S, D]  dtype  (out)   lse  [B, Hq, S]      fp32, natural log (out)
+ *   Hq % Hkv == 0, D == 128, window >= 1, scale > 0 (finite).
+ * --------------------------------------------------------------------------------- */
+int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink,
+                  void* o, float* lse,
+                  int B, int Hq, int Hkv, int S, int D, int window, float scale,
+                  int dtype, void* stream);
+
+/* Workspace bytes attn_sink_bwd needs (0 on invalid sizes).  Layout (offsets in bytes):
+ *   0:                 Delta [B, Hq, S] fp32  (Delta_i = dO_i . O_i; readable after the call)
+ *   align256(4*B*Hq*S): dsink partials [B, Hq, ceil(S/64)] fp32 */
+size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
+
+/* ---------------------------------------------------------------------------------
+ * (A) attn_sink_bwd: backward pass with sink and sliding window.
+ *   q, o, dout [B, Hq, S, D] dtype;  k, v [B, Hkv, S, D] dtype
+ *   lse [B, Hq, S] fp32 (as produced by the forward: includes the sink)
+ *   sink [Hq] fp32
+ *   dq [B, Hq, S, D], dk/dv [B, Hkv, S, D] dtype (out); dsink [Hq] fp32 (out)
+ *   workspace: device buffer of >= attn_sink_bwd_workspace_bytes() bytes, 256-aligned.
+ * Results are deterministic: no atomics; every reduction has a fixed order.
+ * --------------------------------------------------------------------------------- */
+int attn_sink_bwd(const void* q, const void* k, const void* v,
+                  const void* o, const void* dout, const float* lse, const float* sink,
+                  void* dq, void* dk, void* dv, float* dsink,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int S, int D, int window, float scale,
+                  int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * (B) blocksparse_build_tables: device-side mask transpose and selection tables.
+ * Page 2, "optimisation 1" and "optimisation 2" (transpose bit-equal to
+ * mask.permute(0,1,3,2); compaction by exclusive prefix count, so entries ascend).
+ *   block_mask [B, N, nqb, nkb] uint8 (nonzero = keep)
+ *   mask_t     [B, N, nkb, nqb] uint8 (out)
+ *   sel_q      [B, N, nqb, nkb] int32 (out): row i lists the kept key blocks, ascending,
+ *                                            then -1;  cnt_q [B, N, nqb] int32 (out)
+ *   sel_k      [B, N, nkb, nqb] int32 (out): row j lists the kept query blocks,
+ *                                            ascending, then -1;  cnt_k [B, N, nkb] (out)
+ * The outputs are bit-exact functions of the mask.
+ * --------------------------------------------------------------------------------- */
+int blocksparse_build_tables(const uint8_t* block_mask, int B, int N, int nqb, int nkb,
+                             uint8_t* mask_t, int32_t* sel_q, int32_t* cnt_q,
+                             int32_t* sel_k, int32_t* cnt_k, void* stream);
+
+/* (B) blocksparse_attn_fwd: block-sparse forward (support call producing O and lse;
+ * empty rows get O = 0 and lse = -inf).  Layouts as blocksparse_attn_bwd; the workspace
+ * (same size query and layout as the backward) receives the mask tables it iterates. */
+int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                         void* o, float* lse, void* workspace, size_t workspace_bytes,
+                         int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
+                         int dtype, void* stream);
+
+/* Workspace bytes blocksparse_attn_bwd needs (0 on invalid sizes).  Layout, each
+ * region starting at a 256-byte boundary, in this order:
+ *   Delta [B, N, Sq] fp32, mask_t [B, N, nkb, nqb] u8, sel_q [B, N, nqb, nkb] i32,
+ *   cnt_q [B, N, nqb] i32, sel_k [B, N, nkb, nqb] i32, cnt_k [B, N, nkb] i32. */
+size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by);
+
+/* ---------------------------------------------------------------------------------
+ * (B) blocksparse_attn_bwd: block-sparse MHA backward.
+ *   q, o, dout [B, N, Sq, D] dtype;  k, v [B, N, Skv, D] dtype;  lse [B, N, Sq] fp32
+ *   block_mask [B, N, ceil(Sq/bx), ceil(Skv/by)] uint8
+ *   dq [B, N, Sq, D], dk/dv [B, N, Skv, D] dtype (out)
+ * Builds the tables (as blocksparse_build_tables) into the workspace, then Delta, dK/dV
+ * (iterating each key block's kept query blocks) and dQ (iterating each query block's
+ * kept key blocks).  Deterministic.
+ * --------------------------------------------------------------------------------- */
+int blocksparse_attn_bwd(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         const uint8_t* block_mask,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
+                         int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Profiling variants: identical work and results to attn_sink_bwd / blocksparse_attn_bwd,
+ * and additionally record caller-created HIP events (hipEvent_t, passed as void*) on
+ * `stream` between the stages, so per-stage device time can be read with
+ * hipEventElapsedTime without a profiler:
+ *   events[0] before the first kernel            events[1] after preprocess (+ dsink/tables)
+ *   events[2] after the dK/dV kernel             events[3] after the dQ kernel
+ * events must point to 4 valid events (MA_EINVAL if events is NULL).
+ * --------------------------------------------------------------------------------- */
+int attn_sink_bwd_timed(const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, const float* sink,
+                        void* dq, void* dk, void* dv, float* dsink,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int S, int D, int window, float scale,
+                        int dtype, void* stream, void* const* events);
+
+int blocksparse_attn_bwd_timed(const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse,
+                               const uint8_t* block_mask,
+                               void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes,
+                               int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
+                               int dtype, void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MASKATTN_H */

@@ -1,0 +1,543 @@
+// Attention backward kernels for gfx950: preprocess (Delta, dsink partials), a fixed-order
+// dsink reduce, a key/value-tile-stationary dK/dV kernel and a query-tile-stationary dQ
+// kernel.  Both main kernels recompute S = scale*Q K^T and P = exp(S - lse) tile by tile
+// (the FlashAttention-style recompute of the five-GEMM backward: S, P, dV += P^T dO,
+// dP = dO V^T, dS = P (dP - Delta), dK += dS^T Q, dQ += dS K), as described on the page
+// "[Example] Add GQA Sink Backward BHSD ..." (commit of the 9->6 kernel revision: QK^T,
+// softmax, dV+dP, dS, dK+dQ; commit of the 4->2 revision: Delta = sum(O*dO), five GEMMs,
+// dSink) and on the page "knowledge(triton) ... #174" (BlockSparseAttentionGrad skeleton:
+// delta, then dq over the q-major table, then dk/dv over the kv-major table).
+//
+// Design on CDNA4, differing from the pages' Ascend kernels:
+//   * dK/dV accumulate in registers of the workgroup that owns the key tile, and dQ in
+//     the workgroup that owns the query tile, so there are no atomics and no fp32
+//     partial buffers: results are bit-identical run to run (the pages' single-kernel
+//     revision accumulated dK/dV with fp32 atomics and a host-side cast).
+//   * P and dS never leave registers: the accumulator tile of S^T (or S) is re-packed in
+//     place as the A/B operand of the next MFMA, with the contraction index permuted to
+//     match (see ma_device.h), and the other operand is read down the columns of the
+//     staged tile with ds_read_b64_tr_b16.
+//   * Q/dO (or K/V) tiles are double-buffered in LDS; the next tile's global loads are
+//     issued before the current tile's MFMAs.
+#include "ma_launch.h"
+#include "ma_tiles.h"
+
+namespace ma {
+
+// ------------------------------------------------------------------------ preprocess
+// Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]  (fp32), one 64-row block per workgroup.
+// With a sink: part[b,h,blk] = sum_{i in blk} exp(sink_h - lse_i) * Delta_i, summed in a
+// fixed order (tree over the 64 rows).
+template <class T, bool SINK>
+__global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ sink, float* __restrict__ delta,
+                                                         float* __restrict__ part, int H, int S, int nblk) {
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, rsub = tid >> 4, ch = tid & 15;
+  __shared__ float sd[64];
+  const size_t head = ((size_t)b * H + h) * (size_t)S;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int row = blk * 64 + pass * 16 + rsub;
+    float acc = 0.f;
+    if (row < S) {
+      const u32x4 x = ld16(o + (head + row) * HD + ch * 8);
+      const u32x4 y = ld16(dout + (head + row) * HD + ch * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(T::lo(x[e]), T::lo(y[e]), acc);
+        acc = fmaf(T::hi(x[e]), T::hi(y[e]), acc);
+      }
+    }
+    acc += __shfl_xor(acc, 8, 16);
+    acc += __shfl_xor(acc, 4, 16);
+    acc += __shfl_xor(acc, 2, 16);
+    acc += __shfl_xor(acc, 1, 16);
+    if (ch == 0) {
+      if (row < S) delta[head + row] = acc;
+      sd[pass * 16 + rsub] = (row < S) ? acc : 0.f;
+    }
+  }
+  if constexpr (SINK) {
+    __syncthreads();
+    if (tid < 64) {
+      const int row = blk * 64 + tid;
+      float v = 0.f;
+      if (row < S) v = expf(sink[h] - lse[head + row]) * sd[tid];
+      v += __shfl_xor(v, 32);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      if (tid == 0) part[((size_t)b * H + h) * nblk + blk] = v;
+    }
+  }
+}
+
+// dsink[h] = - sum_b sum_blk part[b,h,blk]: one wave per head, fixed order.
+__global__ __launch_bounds__(64) void dsink_reduce_kernel(const float* __restrict__ part, float* __restrict__ dsink,
+                                                          int B, int H, int nblk) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int i = lane; i < nblk; i += 64) acc += part[((size_t)b * H + h) * nblk + i];
+  acc += __shfl_xor(acc, 32);
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (lane == 0) dsink[h] = -acc;
+}
+
+// ------------------------------------------------------------------ tile sources
+// Sequence of (query head, 64-row tile, row bitmask) a stationary workgroup visits.
+struct WindowSource {
+  int head0, nheads, tlo, nt, it;
+  __device__ bool next(int& head, int& tile, uint64_t& bits) {
+    if (it >= nheads * nt) return false;
+    head = head0 + it / nt;
+    tile = tlo + it % nt;
+    bits = 0;
+    ++it;
+    return true;
+  }
+};
+
+struct BlockSource {
+  TileWalker walk;
+  int head;
+  __device__ bool next(int& hd, int& tile, uint64_t& bits) {
+    hd = head;
+    return walk.next(tile, bits);
+  }
+};
+
+// ----------------------------------------------------------------------- dK / dV
+// Workgroup = NW waves owning 32*NW consecutive key rows (wave w: rows c0+32w .. +32).
+// Per visited (head, query tile of 64 rows):
+//   S[q][kv]  = Q K^T          A = Q rows (LDS),   B = K rows (registers)
+//   dP[q][kv] = dO V^T         A = dO rows (LDS),  B = V rows (registers)
+//   P = exp2(S*scale*log2e - lse*log2e), dS = P (dP - Delta)   (accumulator layout:
+//       lane column = key row, registers = query rows)
+//   dV[kv][d] += P^T dO        A = P^T (repacked accumulator), B = dO columns (tr read)
+//   dK[kv][d] += dS^T Q        A = dS^T,                       B = Q columns (tr read)
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kb,
+                                          uint16_t (*sQ)[TILE_ELEMS], uint16_t (*sO)[TILE_ELEMS],
+                                          float (*sL)[64], float (*sD)[64]) {
+  constexpr int NT = NW * 64;
+  constexpr int BC = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+
+  // This lane's key row (clamped into the sequence; rows past the end are never stored).
+  const int kr = min(c0 + 32 * w + c, a.Skv - 1);
+  u32x4 kf[8], vf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kf[ks] = ld16(Kp + (size_t)kr * HD + ks * 16 + 8 * h);
+    vf[ks] = ld16(Vp + (size_t)kr * HD + ks * 16 + 8 * h);
+  }
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    dk[nb] = zero16();
+    dv[nb] = zero16();
+  }
+
+  // Visit order.
+  WindowSource wsrc{};
+  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  if constexpr (MASK == MASK_WINDOW) {
+    const int qend = min(a.Sq, c0 + BC + a.window - 1);
+    const int tlo = c0 >> 6;
+    const int thi = (qend + 63) >> 6;
+    wsrc = WindowSource{kvh * a.group, a.group, tlo, max(0, thi - tlo), 0};
+  } else {
+    const size_t row = kvhead * a.nkb + kb;
+    bsrc = BlockSource{TileWalker(a.sel_k + row * a.nqb, a.cnt_k[row], a.bx, a.Sq), kvh};
+  }
+  auto next = [&](int& hd, int& t, uint64_t& bits) -> bool {
+    if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
+    else return bsrc.next(hd, t, bits);
+  };
+
+  TileStage<NT> stq, sto;
+  constexpr int LPT = (128 + NT - 1) / NT;
+  float stl[LPT];
+  auto load = [&](int hd, int t) {
+    const size_t qhead = (size_t)b * a.Hq + hd;
+    const uint16_t* Qp = (const uint16_t*)a.q + qhead * a.Sq * HD;
+    const uint16_t* Op = (const uint16_t*)a.dout + qhead * a.Sq * HD;
+    stq.load(Qp, t * 64, a.Sq, tid);
+    sto.load(Op, t * 64, a.Sq, tid);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < 128) {
+        const int row = min(t * 64 + (idx & 63), a.Sq - 1);
+        stl[i] = (idx < 64) ? a.lse[qhead * a.Sq + row] * LOG2E : a.delta[qhead * a.Sq + row];
+      }
+    }
+  };
+
+  int hn = 0, tn = 0;
+  uint64_t bn = 0;
+  bool have = next(hn, tn, bn);
+  if (have) load(hn, tn);
+  int buf = 0;
+  const float sl2 = a.scale_log2;
+  const WindowVis wv{a.Sq, a.Skv, a.window};
+  while (have) {
+    const int t = tn;
+    const uint64_t bits = bn;
+    stq.store(sQ[buf], tid);
+    sto.store(sO[buf], tid);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < 64) sL[buf][idx] = stl[i];
+      else if (idx < 128) sD[buf][idx - 64] = stl[i];
+    }
+    __syncthreads();
+    have = next(hn, tn, bn);
+    if (have) load(hn, tn);
+
+    const uint16_t* tq = sQ[buf];
+    const uint16_t* to = sO[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = zero16();
+      dp[mb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s[mb] = T::mma(frag_row(tq, mb * 32 + c, ks, h), kf[ks], s[mb]);
+        dp[mb] = T::mma(frag_row(to, mb * 32 + c, ks, h), vf[ks], dp[mb]);
+      }
+    }
+    const int q0 = t * 64;
+    bool full;
+    if constexpr (MASK == MASK_WINDOW) full = wv.full(q0, 64, c0, BC);
+    else full = (bits == ~0ull);
+    const int kj = c0 + 32 * w + c;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qo = mb * 32 + 8 * g4 + 4 * h;
+        const float4 L = *reinterpret_cast<const float4*>(&sL[buf][qo]);
+        const float4 Dd = *reinterpret_cast<const float4*>(&sD[buf][qo]);
+        const float Lv[4] = {L.x, L.y, L.z, L.w};
+        const float Dv[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float p = fast_exp2(s[mb][r] * sl2 - Lv[e]);
+          if (!full) {
+            bool vis;
+            if constexpr (MASK == MASK_WINDOW) vis = wv.vis(q0 + qo + e, kj);
+            else vis = (bits >> (qo + e)) & 1ull;
+            p = vis ? p : 0.f;
+          }
+          s[mb][r] = p;
+          dp[mb][r] = p * (dp[mb][r] - Dv[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const u32x4 pa = pack8<T>(s[t4 >> 1], 8 * (t4 & 1));
+      const u32x4 da = pack8<T>(dp[t4 >> 1], 8 * (t4 & 1));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        dv[nb] = T::mma(pa, frag_col(to, t4, nb * 32, lane), dv[nb]);
+        dk[nb] = T::mma(da, frag_col(tq, t4, nb * 32, lane), dk[nb]);
+      }
+    }
+    buf ^= 1;
+  }
+
+  // Epilogue: rows c0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
+  uint16_t* dVp = (uint16_t*)a.dv + kvhead * a.Skv * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = c0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < kv_end) {
+        dKp[(size_t)row * HD + nb * 32 + c] = T::one(dk[nb][r] * a.scale);
+        dVp[(size_t)row * HD + nb * 32 + c] = T::one(dv[nb][r]);
+      }
+    }
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64) void dkdv_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sD[2][64];
+  const int nbh = a.B * a.Hkv;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BC = 32 * NW;
+    dkdv_tile<T, MASK, NW>(a, b, kvh, p * BC, a.Skv, 0, sQ, sO, sL, sD);
+    const int p2 = a.n_tiles - 1 - p;
+    if (a.pair && p2 != p) {
+      __syncthreads();
+      dkdv_tile<T, MASK, NW>(a, b, kvh, p2 * BC, a.Skv, 0, sQ, sO, sL, sD);
+    }
+  } else {
+    const int c0 = p * a.by;
+    dkdv_tile<T, MASK, NW>(a, b, kvh, c0, min(c0 + a.by, a.Skv), p, sQ, sO, sL, sD);
+  }
+}
+
+// --------------------------------------------------------------------------- dQ
+// Workgroup = NW waves owning 32*NW consecutive query rows (wave w: rows r0+32w .. +32).
+// Per visited key tile of 64 rows:
+//   S^T[kv][q]  = K Q^T       A = K rows (LDS),  B = Q rows (registers)
+//   dP^T[kv][q] = V dO^T      A = V rows (LDS),  B = dO rows (registers)
+//   (accumulator layout: lane column = query row, registers = key rows)
+//   dQ[q][d] += dS K          A = dS (repacked accumulator), B = K columns (tr read)
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
+                                        uint16_t (*sK)[TILE_ELEMS], uint16_t (*sV)[TILE_ELEMS]) {
+  constexpr int NT = NW * 64;
+  constexpr int BQ = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  const int kvh = hq / a.group;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+
+  const int qi = r0 + 32 * w + c;
+  const int qr = min(qi, a.Sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
+  const uint16_t* Op = (const uint16_t*)a.dout + (qhead * a.Sq + qr) * HD;
+  u32x4 qf[8], of[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = ld16(Qp + ks * 16 + 8 * h);
+    of[ks] = ld16(Op + ks * 16 + 8 * h);
+  }
+  const float l2 = a.lse[qhead * a.Sq + qr] * LOG2E;
+  const float dd = a.delta[qhead * a.Sq + qr];
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+
+  WindowSource wsrc{};
+  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  if constexpr (MASK == MASK_WINDOW) {
+    const int lo = max(0, r0 - a.window + 1);
+    const int hi = min(a.Skv, r0 + BQ);
+    const int tlo = lo >> 6, thi = (hi + 63) >> 6;
+    wsrc = WindowSource{0, 1, tlo, max(0, thi - tlo), 0};
+  } else {
+    const size_t row = qhead * a.nqb + qb;
+    bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
+  }
+  auto next = [&](int& hd, int& t, uint64_t& bits) -> bool {
+    if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
+    else return bsrc.next(hd, t, bits);
+  };
+
+  TileStage<NT> stk, stv;
+  int hn = 0, tn = 0;
+  uint64_t bn = 0;
+  bool have = next(hn, tn, bn);
+  if (have) {
+    stk.load(Kp, tn * 64, a.Skv, tid);
+    stv.load(Vp, tn * 64, a.Skv, tid);
+  }
+  int buf = 0;
+  const float sl2 = a.scale_log2;
+  const WindowVis wv{a.Sq, a.Skv, a.window};
+  while (have) {
+    const int t = tn;
+    const uint64_t bits = bn;
+    stk.store(sK[buf], tid);
+    stv.store(sV[buf], tid);
+    __syncthreads();
+    have = next(hn, tn, bn);
+    if (have) {
+      stk.load(Kp, tn * 64, a.Skv, tid);
+      stv.load(Vp, tn * 64, a.Skv, tid);
+    }
+    const uint16_t* tk = sK[buf];
+    const uint16_t* tv = sV[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = zero16();
+      dp[mb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s[mb] = T::mma(frag_row(tk, mb * 32 + c, ks, h), qf[ks], s[mb]);
+        dp[mb] = T::mma(frag_row(tv, mb * 32 + c, ks, h), of[ks], dp[mb]);
+      }
+    }
+    const int k0 = t * 64;
+    bool full;
+    if constexpr (MASK == MASK_WINDOW) full = wv.full(r0, BQ, k0, 64);
+    else full = (bits == ~0ull);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        float p = fast_exp2(s[mb][r] * sl2 - l2);
+        if (!full) {
+          bool vis;
+          if constexpr (MASK == MASK_WINDOW) vis = wv.vis(qi, k0 + ko);
+          else vis = (bits >> ko) & 1ull;
+          p = vis ? p : 0.f;
+        }
+        dp[mb][r] = p * (dp[mb][r] - dd);
+      }
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const u32x4 da = pack8<T>(dp[t4 >> 1], 8 * (t4 & 1));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(da, frag_col(tk, t4, nb * 32, lane), acc[nb]);
+    }
+    buf ^= 1;
+  }
+
+  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
+    }
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE_ELEMS];
+  const int nbh = a.B * a.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hq, hq = bh % a.Hq;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BQ = 32 * NW;
+    // Heaviest query tiles (most visible keys) are dispatched first.
+    const int t1 = a.n_tiles - 1 - p;
+    dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, sK, sV);
+    const int t2 = p;
+    if (a.pair && t2 != t1) {
+      __syncthreads();
+      dq_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, sK, sV);
+    }
+  } else {
+    const int r0 = p * a.bx;
+    dq_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, sK, sV);
+  }
+}
+
+// ------------------------------------------------------------------------ launchers
+template <class T>
+static hipError_t launch_preprocess_t(const void* o, const void* dout, const float* lse, const float* sink,
+                                      float* delta, float* part, int B, int H, int S, hipStream_t st) {
+  const int nblk = (S + 63) / 64;
+  dim3 grid(nblk, H, B);
+  if (sink)
+    hipLaunchKernelGGL((preprocess_kernel<T, true>), grid, dim3(256), 0, st, (const uint16_t*)o,
+                       (const uint16_t*)dout, lse, sink, delta, part, H, S, nblk);
+  else
+    hipLaunchKernelGGL((preprocess_kernel<T, false>), grid, dim3(256), 0, st, (const uint16_t*)o,
+                       (const uint16_t*)dout, lse, sink, delta, part, H, S, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(int dtype, const void* o, const void* dout, const float* lse, const float* sink,
+                             float* delta, float* part, int B, int H, int S, hipStream_t st) {
+  return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, part, B, H, S, st)
+                    : launch_preprocess_t<F16>(o, dout, lse, sink, delta, part, B, H, S, st);
+}
+
+hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, int S, hipStream_t st) {
+  const int nblk = (S + 63) / 64;
+  hipLaunchKernelGGL(dsink_reduce_kernel, dim3(H), dim3(64), 0, st, part, dsink, B, H, nblk);
+  return hipGetLastError();
+}
+
+template <class T, int MASK, int NW>
+static void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+}
+
+template <class T, int MASK, int NW>
+static void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dq_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+}
+
+hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid) {
+  // Key/value tiles of 128 rows (dK/dV) and query tiles of 128 rows (dQ).  When the
+  // window is wide the work per tile grows linearly along the sequence, so a workgroup
+  // runs tile p and tile n-1-p (equal total work) whenever that still leaves at least
+  // one workgroup per compute unit.
+  const int nt = (a.Skv + 127) / 128;
+  const bool wide = a.window >= 256 && a.window * 4 >= a.Skv;
+  const int pairs_dkdv = a.B * a.Hkv * ((nt + 1) / 2);
+  const int pairs_dq = a.B * a.Hq * ((nt + 1) / 2);
+  AttnArgs ak = a, aq = a;
+  ak.n_tiles = nt;
+  aq.n_tiles = (a.Sq + 127) / 128;
+  ak.pair = (wide && pairs_dkdv >= 256) ? 1 : 0;
+  aq.pair = (wide && pairs_dq >= 256) ? 1 : 0;
+  const int gk = a.B * a.Hkv * (ak.pair ? (ak.n_tiles + 1) / 2 : ak.n_tiles);
+  const int gq = a.B * a.Hq * (aq.pair ? (aq.n_tiles + 1) / 2 : aq.n_tiles);
+  if (dtype == 1) launch_dkdv_only<BF16, MASK_WINDOW, 4>(ak, gk, st);
+  else launch_dkdv_only<F16, MASK_WINDOW, 4>(ak, gk, st);
+  if (ev_mid) hipEventRecord(ev_mid, st);
+  if (dtype == 1) launch_dq_only<BF16, MASK_WINDOW, 4>(aq, gq, st);
+  else launch_dq_only<F16, MASK_WINDOW, 4>(aq, gq, st);
+  return hipGetLastError();
+}
+
+template <class T>
+static void launch_block_t(const AttnArgs& a, hipStream_t st, hipEvent_t ev_mid) {
+  const int nwk = (a.by + 31) / 32, nwq = (a.bx + 31) / 32;
+  const int gk = a.B * a.Hkv * a.nkb, gq = a.B * a.Hq * a.nqb;
+  switch (nwk) {
+    case 1: launch_dkdv_only<T, MASK_BLOCK, 1>(a, gk, st); break;
+    case 2: launch_dkdv_only<T, MASK_BLOCK, 2>(a, gk, st); break;
+    case 3: launch_dkdv_only<T, MASK_BLOCK, 3>(a, gk, st); break;
+    default: launch_dkdv_only<T, MASK_BLOCK, 4>(a, gk, st); break;
+  }
+  if (ev_mid) hipEventRecord(ev_mid, st);
+  switch (nwq) {
+    case 1: launch_dq_only<T, MASK_BLOCK, 1>(a, gq, st); break;
+    case 2: launch_dq_only<T, MASK_BLOCK, 2>(a, gq, st); break;
+    case 3: launch_dq_only<T, MASK_BLOCK, 3>(a, gq, st); break;
+    default: launch_dq_only<T, MASK_BLOCK, 4>(a, gq, st); break;
+  }
+}
+
+hipError_t launch_block_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid) {
+  if (dtype == 1) launch_block_t<BF16>(a, st, ev_mid);
+  else launch_block_t<F16>(a, st, ev_mid);
+  return hipGetLastError();
+}
+
+}  // namespace ma

@@ -1,0 +1,219 @@
+// Attention forward for gfx950 with a sink logit and a sliding causal window, or with a
+// block mask: O and the natural-log lse that the backward consumes.  Page "[Example] Add
+// GQA Sink Backward BHSD ..." ("Files Added": online softmax with an attention sink and a
+// sliding-window mask; commit of the 4->2 revision: forward -> O, lse).
+//
+// Online softmax per query row, started from the sink: running max m = sink and running
+// sum l = 1 (m = -inf, l = 0 without a sink), then every visible key tile rescales and
+// accumulates.  lse = m + log(l) therefore includes the sink, and a row that sees
+// nothing ends with O = 0, lse = -inf.
+//
+// Workgroup = NW waves owning 32*NW query rows; per 64-row key tile:
+//   S^T[kv][q] = K Q^T      A = K rows (LDS), B = Q rows (registers); lane column = query
+//   O^T[d][q] += V^T P^T    A = V columns (tr read), B = P^T (repacked accumulator)
+// Accumulating O transposed keeps each lane's registers on its own query row, so the
+// rescale by exp(m_old - m_new) is one multiply per register with no data exchange.
+#include "ma_launch.h"
+#include "ma_tiles.h"
+
+namespace ma {
+
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
+                                         uint16_t (*sK)[TILE_ELEMS], uint16_t (*sV)[TILE_ELEMS]) {
+  constexpr int NT = NW * 64;
+  constexpr int BQ = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  const int kvh = hq / a.group;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+
+  const int qi = r0 + 32 * w + c;
+  const int qr = min(qi, a.Sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
+  u32x4 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = ld16(Qp + ks * 16 + 8 * h);
+
+  float m2 = -INFINITY, l = 0.f;   // running max (log2 domain) and sum
+  if constexpr (MASK == MASK_WINDOW) {
+    if (a.sink) {
+      const float sk = a.sink[hq];
+      if (sk > -INFINITY) {
+        m2 = sk * LOG2E;
+        l = 1.f;
+      }
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+
+  int tlo = 0, nt = 0;
+  TileWalker walk(nullptr, 0, 1, 1);
+  if constexpr (MASK == MASK_WINDOW) {
+    const int lo = max(0, r0 - a.window + 1);
+    const int hi = min(a.Skv, r0 + BQ);
+    tlo = lo >> 6;
+    nt = max(0, ((hi + 63) >> 6) - tlo);
+  } else {
+    const size_t row = qhead * a.nqb + qb;
+    walk = TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv);
+  }
+  int it = 0;
+  auto next = [&](int& t, uint64_t& bits) -> bool {
+    if constexpr (MASK == MASK_WINDOW) {
+      if (it >= nt) return false;
+      t = tlo + it++;
+      bits = 0;
+      return true;
+    } else {
+      return walk.next(t, bits);
+    }
+  };
+
+  TileStage<NT> stk, stv;
+  int tn = 0;
+  uint64_t bn = 0;
+  bool have = next(tn, bn);
+  if (have) {
+    stk.load(Kp, tn * 64, a.Skv, tid);
+    stv.load(Vp, tn * 64, a.Skv, tid);
+  }
+  int buf = 0;
+  const float sl2 = a.scale_log2;
+  const WindowVis wv{a.Sq, a.Skv, a.window};
+  while (have) {
+    const int t = tn;
+    const uint64_t bits = bn;
+    stk.store(sK[buf], tid);
+    stv.store(sV[buf], tid);
+    __syncthreads();
+    have = next(tn, bn);
+    if (have) {
+      stk.load(Kp, tn * 64, a.Skv, tid);
+      stv.load(Vp, tn * 64, a.Skv, tid);
+    }
+    const uint16_t* tk = sK[buf];
+    const uint16_t* tv = sV[buf];
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s[mb] = T::mma(frag_row(tk, mb * 32 + c, ks, h), qf[ks], s[mb]);
+    }
+    const int k0 = t * 64;
+    bool full;
+    if constexpr (MASK == MASK_WINDOW) full = wv.full(r0, BQ, k0, 64);
+    else full = (bits == ~0ull);
+    // Scaled logits in the log2 domain; hidden entries become -inf.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        float x = s[mb][r] * sl2;
+        if (!full) {
+          bool vis;
+          if constexpr (MASK == MASK_WINDOW) vis = wv.vis(qi, k0 + ko);
+          else vis = (bits >> ko) & 1ull;
+          x = vis ? x : -INFINITY;
+        }
+        s[mb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m2, mx);
+    const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+    float rs = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // A finite logit implies a finite running max no smaller than it.
+        const float p = (s[mb][r] == -INFINITY) ? 0.f : fast_exp2(s[mb][r] - mnew);
+        s[mb][r] = p;
+        rs += p;
+      }
+    }
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m2 = mnew;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const u32x4 pb = pack8<T>(s[t4 >> 1], 8 * (t4 & 1));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(frag_col(tv, t4, nb * 32, lane), pb, acc[nb]);
+    }
+    buf ^= 1;
+  }
+
+  // Epilogue: lane (c, h) holds O^T[d = nb*32 + 8(r/4) + 4h + r%4][q = qi].
+  if (qi < q_end) {
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    uint16_t* Orow = (uint16_t*)a.out_o + (qhead * a.Sq + qi) * HD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 v;
+        v[0] = T::pack2(acc[nb][4 * g4 + 0] * inv, acc[nb][4 * g4 + 1] * inv);
+        v[1] = T::pack2(acc[nb][4 * g4 + 2] * inv, acc[nb][4 * g4 + 3] * inv);
+        st8(Orow + nb * 32 + 8 * g4 + 4 * h, v);
+      }
+    }
+    if (h == 0) a.out_lse[qhead * a.Sq + qi] = (l > 0.f) ? (m2 + __log2f(l)) * LN2 : -INFINITY;
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE_ELEMS];
+  const int nbh = a.B * a.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hq, hq = bh % a.Hq;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BQ = 32 * NW;
+    const int t1 = a.n_tiles - 1 - p;
+    fwd_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, sK, sV);
+  } else {
+    const int r0 = p * a.bx;
+    fwd_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, sK, sV);
+  }
+}
+
+template <class T>
+static void launch_fwd_t(const AttnArgs& a, int mask, hipStream_t st) {
+  if (mask == MASK_WINDOW) {
+    AttnArgs w = a;
+    w.n_tiles = (a.Sq + 127) / 128;
+    hipLaunchKernelGGL((fwd_kernel<T, MASK_WINDOW, 4>), dim3(a.B * a.Hq * w.n_tiles), dim3(256), 0, st, w);
+    return;
+  }
+  const int g = a.B * a.Hq * a.nqb;
+  switch ((a.bx + 31) / 32) {
+    case 1: hipLaunchKernelGGL((fwd_kernel<T, MASK_BLOCK, 1>), dim3(g), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((fwd_kernel<T, MASK_BLOCK, 2>), dim3(g), dim3(128), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((fwd_kernel<T, MASK_BLOCK, 3>), dim3(g), dim3(192), 0, st, a); break;
+    default: hipLaunchKernelGGL((fwd_kernel<T, MASK_BLOCK, 4>), dim3(g), dim3(256), 0, st, a); break;
+  }
+}
+
+hipError_t launch_fwd(int dtype, AttnArgs a, int mask, hipStream_t st) {
+  if (dtype == 1) launch_fwd_t<BF16>(a, mask, st);
+  else launch_fwd_t<F16>(a, mask, st);
+  return hipGetLastError();
+}
+
+}  // namespace ma

@@ -1,0 +1,299 @@
+// C ABI of the masked attention library: host-side validation of scalars and pointer
+// values, workspace carving, and kernel enqueueing on the caller's stream.
+//
+// The host does shapes, offsets and launches only (page "knowledge(triton) ... #174",
+// BlockSparseAttentionGrad runbook, "optimisation 1": the host only checks shapes,
+// allocates and views).  Nothing here reads device memory, allocates, or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "maskattn.h"
+#include "ma_launch.h"
+
+using ma::AttnArgs;
+
+namespace {
+
+constexpr int kMaxDim = 65535;    // grid y/z limits of the preprocess launch
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+// Rows of one [B, H, S] tensor must stay well inside int32 grid/row arithmetic.
+bool sizes_fit(long long B, long long H, long long S) {
+  return B * H * S <= (1ll << 31) - 1 && B * H * ((S + 63) / 64) <= (1ll << 31) - 1;
+}
+
+int check_common(int B, int Hq, int Hkv, int S, int D, float scale, int dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return MA_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return MA_EINVAL;
+  if (Hq % Hkv != 0) return MA_EINVAL;
+  if (D != ma::HD) return MA_EUNSUPPORTED;
+  if (dtype != MA_F16 && dtype != MA_BF16) return MA_EUNSUPPORTED;
+  if (B > kMaxDim || Hq > kMaxDim) return MA_EUNSUPPORTED;
+  if (!sizes_fit(B, Hq, S)) return MA_EUNSUPPORTED;
+  return MA_OK;
+}
+
+int check_blocks(int bx, int by) {
+  if (bx < 1 || by < 1) return MA_EINVAL;
+  if (bx % 16 != 0 || by % 16 != 0 || bx > 128 || by > 128) return MA_EUNSUPPORTED;
+  return MA_OK;
+}
+
+struct BlockLayout {
+  size_t delta, mask_t, sel_q, cnt_q, sel_k, cnt_k, total;
+};
+
+BlockLayout block_layout(int B, int N, int Sq, int nqb, int nkb) {
+  BlockLayout l;
+  const size_t bn = (size_t)B * N;
+  l.delta = 0;
+  l.mask_t = align256(l.delta + bn * Sq * sizeof(float));
+  l.sel_q = align256(l.mask_t + bn * nkb * nqb);
+  l.cnt_q = align256(l.sel_q + bn * nqb * nkb * sizeof(int32_t));
+  l.sel_k = align256(l.cnt_q + bn * nqb * sizeof(int32_t));
+  l.cnt_k = align256(l.sel_k + bn * nkb * nqb * sizeof(int32_t));
+  l.total = align256(l.cnt_k + bn * nkb * sizeof(int32_t));
+  return l;
+}
+
+AttnArgs base_args(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Sq, int Skv,
+                   float scale) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.group = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return a;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MA_OK : MA_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* maskattn_strerror(int status) {
+  switch (status) {
+    case MA_OK: return "ok";
+    case MA_EINVAL: return "invalid argument (null or misaligned pointer, bad size, Hq % Hkv != 0, window < 1)";
+    case MA_EUNSUPPORTED: return "unsupported configuration (D != 128, block size, dtype or size limits)";
+    case MA_EWORKSPACE: return "workspace too small";
+    case MA_ELAUNCH: return "HIP runtime error while enqueueing";
+    default: return "unknown status";
+  }
+}
+
+int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink, void* o, float* lse, int B,
+                  int Hq, int Hkv, int S, int D, int window, float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, S, D, scale, dtype);
+  if (st) return st;
+  if (window < 1) return MA_EINVAL;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return MA_EINVAL;
+  if (!sink || !aligned(sink, 4) || !lse || !aligned(lse, 4)) return MA_EINVAL;
+  AttnArgs a = base_args(q, k, v, B, Hq, Hkv, S, S, scale);
+  a.sink = sink;
+  a.out_o = o;
+  a.out_lse = lse;
+  a.window = window < S ? window : S;
+  return status_of(ma::launch_fwd(dtype, a, ma::MASK_WINDOW, (hipStream_t)stream));
+}
+
+size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+  if (check_common(B, Hq, Hkv, S, D, 1.f, MA_F16) != MA_OK) return 0;
+  const size_t rows = (size_t)B * Hq * S;
+  const size_t nblk = (size_t)B * Hq * ((S + 63) / 64);
+  return align256(align256(rows * sizeof(float)) + nblk * sizeof(float));
+}
+
+static int sink_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink,
+                         void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int window,
+                         float scale, int dtype, void* stream, void* const* events) {
+  int st = check_common(B, Hq, Hkv, S, D, scale, dtype);
+  if (st) return st;
+  if (window < 1) return MA_EINVAL;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) || !tensor_ok(dq) ||
+      !tensor_ok(dk) || !tensor_ok(dv))
+    return MA_EINVAL;
+  if (!lse || !aligned(lse, 4) || !sink || !aligned(sink, 4) || !dsink || !aligned(dsink, 4)) return MA_EINVAL;
+  if (!workspace || !aligned(workspace, 256)) return MA_EINVAL;
+  const size_t need = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D);
+  if (workspace_bytes < need) return MA_EWORKSPACE;
+  hipStream_t hs = (hipStream_t)stream;
+  float* delta = at<float>(workspace, 0);
+  float* part = at<float>(workspace, align256((size_t)B * Hq * S * sizeof(float)));
+
+  if (events) hipEventRecord((hipEvent_t)events[0], hs);
+  hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, part, B, Hq, S, hs);
+  if (e != hipSuccess) return MA_ELAUNCH;
+  e = ma::launch_dsink_reduce(part, dsink, B, Hq, S, hs);
+  if (e != hipSuccess) return MA_ELAUNCH;
+  if (events) hipEventRecord((hipEvent_t)events[1], hs);
+  AttnArgs a = base_args(q, k, v, B, Hq, Hkv, S, S, scale);
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.sink = sink;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.window = window < S ? window : S;
+  e = ma::launch_window_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
+  if (events) hipEventRecord((hipEvent_t)events[3], hs);
+  return status_of(e);
+}
+
+int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  const float* sink, void* dq, void* dk, void* dv, float* dsink, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int window, float scale, int dtype,
+                  void* stream) {
+  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, workspace, workspace_bytes, B, Hq, Hkv, S, D,
+                       window, scale, dtype, stream, nullptr);
+}
+
+int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink,
+                        void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int window,
+                        float scale, int dtype, void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return MA_EINVAL;
+  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, workspace, workspace_bytes, B, Hq, Hkv, S, D,
+                       window, scale, dtype, stream, events);
+}
+
+int blocksparse_build_tables(const uint8_t* block_mask, int B, int N, int nqb, int nkb, uint8_t* mask_t,
+                             int32_t* sel_q, int32_t* cnt_q, int32_t* sel_k, int32_t* cnt_k, void* stream) {
+  if (B < 1 || N < 1 || nqb < 1 || nkb < 1) return MA_EINVAL;
+  if (B > kMaxDim || N > kMaxDim || (long long)B * N > (1ll << 31) - 1) return MA_EUNSUPPORTED;
+  if ((long long)nqb * nkb > (1ll << 30)) return MA_EUNSUPPORTED;
+  if (!block_mask || !mask_t || !sel_q || !cnt_q || !sel_k || !cnt_k) return MA_EINVAL;
+  if (!aligned(sel_q, 4) || !aligned(cnt_q, 4) || !aligned(sel_k, 4) || !aligned(cnt_k, 4)) return MA_EINVAL;
+  return status_of(ma::launch_mask_tables(block_mask, B * N, nqb, nkb, mask_t, sel_q, cnt_q, sel_k, cnt_k,
+                                          (hipStream_t)stream));
+}
+
+size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by) {
+  if (check_common(B, N, N, Sq, D, 1.f, MA_F16) != MA_OK || Skv < 1 || check_blocks(bx, by) != MA_OK) return 0;
+  if (!sizes_fit(B, N, Skv)) return 0;
+  const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
+  return block_layout(B, N, Sq, nqb, nkb).total;
+}
+
+static int block_common(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* workspace,
+                        size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
+                        int dtype) {
+  int st = check_common(B, N, N, Sq, D, scale, dtype);
+  if (st) return st;
+  if (Skv < 1) return MA_EINVAL;
+  if (!sizes_fit(B, N, Skv)) return MA_EUNSUPPORTED;
+  st = check_blocks(bx, by);
+  if (st) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !block_mask) return MA_EINVAL;
+  if (!workspace || !aligned(workspace, 256)) return MA_EINVAL;
+  if (workspace_bytes < blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, D, bx, by)) return MA_EWORKSPACE;
+  return MA_OK;
+}
+
+int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
+                         int by, float scale, int dtype, void* stream) {
+  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, N, Sq, Skv, D, bx, by, scale, dtype);
+  if (st) return st;
+  if (!tensor_ok(o) || !lse || !aligned(lse, 4)) return MA_EINVAL;
+  const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
+  const BlockLayout L = block_layout(B, N, Sq, nqb, nkb);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = ma::launch_mask_tables(block_mask, B * N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
+                                        at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
+                                        at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), hs);
+  if (e != hipSuccess) return MA_ELAUNCH;
+  AttnArgs a = base_args(q, k, v, B, N, N, Sq, Skv, scale);
+  a.out_o = o;
+  a.out_lse = lse;
+  a.mask = block_mask;
+  a.sel_q = at<int>(workspace, L.sel_q);
+  a.cnt_q = at<int>(workspace, L.cnt_q);
+  a.sel_k = at<int>(workspace, L.sel_k);
+  a.cnt_k = at<int>(workspace, L.cnt_k);
+  a.bx = bx;
+  a.by = by;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  return status_of(ma::launch_fwd(dtype, a, ma::MASK_BLOCK, hs));
+}
+
+static int block_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
+                          int by, float scale, int dtype, void* stream, void* const* events) {
+  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, N, Sq, Skv, D, bx, by, scale, dtype);
+  if (st) return st;
+  if (!tensor_ok(o) || !tensor_ok(dout) || !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv)) return MA_EINVAL;
+  if (!lse || !aligned(lse, 4)) return MA_EINVAL;
+  const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
+  const BlockLayout L = block_layout(B, N, Sq, nqb, nkb);
+  hipStream_t hs = (hipStream_t)stream;
+  if (events) hipEventRecord((hipEvent_t)events[0], hs);
+  hipError_t e = ma::launch_mask_tables(block_mask, B * N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
+                                        at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
+                                        at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), hs);
+  if (e != hipSuccess) return MA_ELAUNCH;
+  float* delta = at<float>(workspace, L.delta);
+  e = ma::launch_preprocess(dtype, o, dout, lse, nullptr, delta, nullptr, B, N, Sq, hs);
+  if (e != hipSuccess) return MA_ELAUNCH;
+  if (events) hipEventRecord((hipEvent_t)events[1], hs);
+  AttnArgs a = base_args(q, k, v, B, N, N, Sq, Skv, scale);
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.mask = block_mask;
+  a.sel_q = at<int>(workspace, L.sel_q);
+  a.cnt_q = at<int>(workspace, L.cnt_q);
+  a.sel_k = at<int>(workspace, L.sel_k);
+  a.cnt_k = at<int>(workspace, L.cnt_k);
+  a.bx = bx;
+  a.by = by;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  e = ma::launch_block_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
+  if (events) hipEventRecord((hipEvent_t)events[3], hs);
+  return status_of(e);
+}
+
+int blocksparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
+                         int dtype, void* stream) {
+  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, Sq, Skv, D,
+                        bx, by, scale, dtype, stream, nullptr);
+}
+
+int blocksparse_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
+                               int by, float scale, int dtype, void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return MA_EINVAL;
+  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, Sq, Skv, D,
+                        bx, by, scale, dtype, stream, events);
+}
+
+}  // extern "C"

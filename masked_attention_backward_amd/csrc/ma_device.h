@@ -1,0 +1,163 @@
+// Device helpers shared by the masked attention kernels (gfx950 / CDNA4 only).
+//
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_{f16,bf16}, wave64):
+//   lane l = 32*h + c  (c = l % 32, h = l / 32)
+//   A operand (32 x 16, M x K): lane l holds row m = c, eight k-slots of half h.
+//   B operand (16 x 32, K x N): lane l holds column n = c, the same eight k-slots.
+//   C/D (32 x 32): lane l, accumulator r in [0,16): row 8*(r/4) + 4*h + (r%4), column c.
+// The contraction pairs A-slot s of half h with B-slot s of half h, so any bijection of
+// (h, s) onto the 16 k indices is valid as long as both operands use the same one.  The
+// kernels exploit that: an accumulator tile (rows spread over registers) is fed back as
+// the A or B operand of the next product with the k index permuted to match.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ma {
+
+constexpr int HD = 128;          // head dimension (the only one supported)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element-type traits: 16-bit storage, fp32 compute.
+struct F16 {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  }
+  static __device__ __forceinline__ uint16_t one(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
+
+struct BF16 {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+  static __device__ __forceinline__ uint16_t one(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Pack eight accumulator values acc[r0 .. r0+7] into one MFMA operand (eight 16-bit slots).
+template <class T>
+__device__ __forceinline__ u32x4 pack8(const f32x16& acc, int r0) {
+  u32x4 o;
+  o[0] = T::pack2(acc[r0 + 0], acc[r0 + 1]);
+  o[1] = T::pack2(acc[r0 + 2], acc[r0 + 3]);
+  o[2] = T::pack2(acc[r0 + 4], acc[r0 + 5]);
+  o[3] = T::pack2(acc[r0 + 6], acc[r0 + 7]);
+  return o;
+}
+
+// Bits [a, b) of a 64-bit word, 0 <= a <= b <= 64.
+__device__ __forceinline__ uint64_t range_bits(int a, int b) {
+  uint64_t hi = (b >= 64) ? ~0ull : ((1ull << b) - 1ull);
+  uint64_t lo = (a >= 64) ? ~0ull : ((1ull << a) - 1ull);
+  return hi & ~lo;
+}
+
+// Walks the 64-row tiles covered by an ascending list of kept blocks (one row of a
+// selection table).  Each visited tile is reported once, in ascending order, with the
+// bitmask of its rows that lie inside a kept block and inside the sequence.
+struct TileWalker {
+  const int* sel;
+  int cnt, blk, len;
+  int idx, last;
+  __device__ TileWalker(const int* sel_, int cnt_, int blk_, int len_)
+      : sel(sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1) {}
+  __device__ bool next(int& tile, uint64_t& bits) {
+    while (idx < cnt) {
+      const int j = sel[idx];
+      const int lo = j * blk;
+      const int hi = min(lo + blk, len);
+      int t = lo >> 6;
+      if (t <= last) t = last + 1;
+      if (t * 64 >= hi) {
+        ++idx;
+        continue;
+      }
+      const int t0 = t * 64, t1 = t0 + 64;
+      uint64_t m = 0;
+      for (int k = idx; k < cnt; ++k) {
+        const int j2 = sel[k];
+        const int lo2 = max(j2 * blk, t0);
+        const int hi2 = min(min(j2 * blk + blk, len), t1);
+        if (j2 * blk >= t1) break;
+        if (lo2 < hi2) m |= range_bits(lo2 - t0, hi2 - t0);
+      }
+      last = t;
+      tile = t;
+      bits = m;
+      return true;
+    }
+    return false;
+  }
+};
+
+// Kernel argument block shared by the attention kernels.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  const float* sink;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* out_o;
+  float* out_lse;
+  const uint8_t* mask;   // [B, N, nqb, nkb]
+  const int* sel_q;      // [B, N, nqb, nkb]
+  const int* cnt_q;      // [B, N, nqb]
+  const int* sel_k;      // [B, N, nkb, nqb]
+  const int* cnt_k;      // [B, N, nkb]
+  int B, Hq, Hkv, Sq, Skv, group;
+  int window;
+  int bx, by, nqb, nkb;
+  float scale, scale_log2;
+  int n_tiles;           // stationary tiles per head (window path)
+  int pair;              // 1: workgroup p also runs tile n_tiles-1-p
+  int wg_per_head;       // workgroups per head along the stationary dimension
+};
+
+enum { MASK_WINDOW = 0, MASK_BLOCK = 1 };
+
+}  // namespace ma

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every symbol include/maskattn.h declares, and rejects
+invalid arguments on the host (these calls return before any GPU work is enqueued)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maskattn.h")
+LIB = os.path.join(ROOT, "masked_attention_backward_amd", "libmaskattn.so")
+
+P = 0x10000          # a fake 64 KiB-aligned pointer value: never dereferenced on these paths
+F16, BF16 = 0, 1
+EINVAL, EUNSUP, EWS = 1, 2, 3
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmaskattn.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_match_header(lib):
+    names = declared()
+    assert "attn_sink_bwd" in names and "blocksparse_attn_bwd" in names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    from masked_attention_backward_amd import api
+    assert set(api.EXPORTS) == set(names)
+
+
+def test_strerror(lib):
+    lib.maskattn_strerror.restype = ctypes.c_char_p
+    for s in range(5):
+        assert lib.maskattn_strerror(s)
+    assert b"unknown" in lib.maskattn_strerror(99)
+
+
+def sink_bwd(lib, B=1, Hq=4, Hkv=1, S=128, D=128, window=64, scale=0.088, dtype=F16, ws_bytes=None, **ptrs):
+    f = lib.attn_sink_bwd
+    V, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    f.argtypes = [V] * 11 + [V, Z] + [I] * 6 + [ctypes.c_float, I, V]
+    names = ["q", "k", "v", "o", "do", "lse", "sink", "dq", "dk", "dv", "dsink", "ws"]
+    vals = [ptrs.get(n, P) for n in names]
+    lib.attn_sink_bwd_workspace_bytes.restype = Z
+    need = lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return f(*vals[:11], vals[11], ws_bytes, B, Hq, Hkv, S, D, window, scale, dtype, None)
+
+
+def test_sink_bwd_validation(lib):
+    assert sink_bwd(lib, D=64) == EUNSUP                      # D=64 is rejected, not silently accepted
+    assert sink_bwd(lib, Hq=4, Hkv=3) == EINVAL
+    assert sink_bwd(lib, window=0) == EINVAL
+    assert sink_bwd(lib, S=0) == EINVAL
+    assert sink_bwd(lib, B=0) == EINVAL
+    assert sink_bwd(lib, scale=0.0) == EINVAL
+    assert sink_bwd(lib, scale=float("nan")) == EINVAL
+    assert sink_bwd(lib, dtype=7) == EUNSUP
+    assert sink_bwd(lib, q=0) == EINVAL
+    assert sink_bwd(lib, dq=P + 8) == EINVAL                 # misaligned tensor
+    assert sink_bwd(lib, dsink=0) == EINVAL
+    assert sink_bwd(lib, ws=P + 128) == EINVAL               # workspace must be 256-aligned
+    assert sink_bwd(lib, ws_bytes=100) == EWS
+
+
+def test_workspace_queries(lib):
+    Z, I = ctypes.c_size_t, ctypes.c_int
+    lib.attn_sink_bwd_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_workspace_bytes.argtypes = [I] * 7
+    n = lib.attn_sink_bwd_workspace_bytes(2, 32, 8, 2048, 128)
+    assert n >= 2 * 32 * 2048 * 4 + 2 * 32 * 32 * 4 and n % 256 == 0
+    assert lib.attn_sink_bwd_workspace_bytes(1, 4, 1, 128, 64) == 0
+    m = lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 80)
+    nqb, nkb = 63, 38
+    assert m >= 2 * 8 * (3000 * 4 + nqb * nkb * 9 + (nqb + nkb) * 4)
+    assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 40, 80) == 0    # bx % 16 != 0
+    assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 144) == 0   # by > 128
+
+
+def test_blocksparse_validation(lib):
+    V, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    f = lib.blocksparse_attn_bwd
+    f.argtypes = [V] * 10 + [V, Z] + [I] * 7 + [F, I, V]
+
+    def call(bx=64, by=64, D=128, Sq=256, Skv=256, ws_bytes=1 << 20, dtype=F16, mask=P):
+        return f(P, P, P, P, P, P, mask, P, P, P, P, ws_bytes, 1, 2, Sq, Skv, D, bx, by, 0.088, dtype, None)
+
+    assert call(bx=40) == EUNSUP
+    assert call(by=256) == EUNSUP
+    assert call(bx=0) == EINVAL
+    assert call(D=96) == EUNSUP
+    assert call(Skv=0) == EINVAL
+    assert call(mask=0) == EINVAL
+    assert call(ws_bytes=16) == EWS
+    t = lib.blocksparse_build_tables
+    t.argtypes = [V, I, I, I, I, V, V, V, V, V, V]
+    assert t(P, 1, 1, 0, 4, P, P, P, P, P, None) == EINVAL
+    assert t(0, 1, 1, 4, 4, P, P, P, P, P, None) == EINVAL

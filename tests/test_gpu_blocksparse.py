@@ -1,0 +1,153 @@
+"""GPU parity of the block-sparse path: tables bit-exact, forward and backward against the oracle."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_attention_backward_amd import workloads as W
+from parity import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def api():
+    from masked_attention_backward_amd import api as a
+    return a
+
+
+def with_oracle_forward(wl, x):
+    o, lse = oracle.blocksparse_attention_forward(x["q"], x["k"], x["v"], x["block_mask"], wl.bx, wl.by, wl.scale)
+    x["o"] = torch.from_numpy(o).to(wl.dtype)
+    x["lse"] = torch.from_numpy(lse).to(torch.float32)
+    return x
+
+
+def gpu_bwd(wl, x):
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] blocksparse_attn_bwd {wl.name} B{wl.B} N{wl.Hq} Sq{wl.Sq} Skv{wl.Skv} bx{wl.bx} by{wl.by}",
+          flush=True)
+    out = api().blocksparse_attn_bwd(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["block_mask"], wl.bx,
+                                     wl.by, wl.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["bigbird", "ragged"])
+def test_tables_bit_exact_workload_masks(name):
+    wl = W.WORKLOADS[name]
+    m = W.make_block_mask(wl)
+    print(f"[gpu] blocksparse_build_tables {name}", flush=True)
+    got = api().blocksparse_build_tables(m.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.build_block_tables(m)
+    for k in ("mask_t", "sel_q", "cnt_q", "sel_k", "cnt_k"):
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+
+
+@pytest.mark.parametrize("shape,density", [((1, 1, 1, 1), 1.0), ((2, 3, 5, 7), 0.4), ((1, 2, 130, 67), 0.3),
+                                           ((1, 1, 64, 200), 0.0), ((1, 1, 129, 1), 0.5)])
+def test_tables_bit_exact_random(shape, density):
+    rng = np.random.default_rng(sum(shape))
+    m = ((rng.random(shape) < density) * rng.integers(1, 256, size=shape)).astype(np.uint8)
+    print(f"[gpu] blocksparse_build_tables {shape}", flush=True)
+    got = api().blocksparse_build_tables(torch.from_numpy(m).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.build_block_tables(m)
+    for k in ("mask_t", "sel_q", "cnt_q", "sel_k", "cnt_k"):
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+
+
+SMALL = [
+    W.custom_blocksparse("b64_bigbird", 1, 2, 512, 512, 64, 64, "bigbird", seed_base=201),
+    W.custom_blocksparse("b48x80_ragged", 1, 2, 300, 300, 48, 80, "ragged", seed_base=202),
+    W.custom_blocksparse("b16x16_random", 1, 2, 200, 170, 16, 16, "random", density=0.3, seed_base=203),
+    W.custom_blocksparse("b128x32_random", 2, 1, 400, 333, 128, 32, "random", density=0.5, seed_base=204),
+    W.custom_blocksparse("b32x128_causal_bf16", 1, 2, 384, 384, 32, 128, "causal", dtype=torch.bfloat16,
+                         seed_base=205),
+    W.custom_blocksparse("b80x48_dense", 1, 1, 250, 260, 80, 48, "dense", seed_base=206),
+    W.custom_blocksparse("b64x96_random_emptyrows", 1, 2, 320, 300, 64, 96, "random", density=0.2, seed_base=207),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_bwd_small(wl):
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv = gpu_bwd(wl, x)
+    ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
+                                                wl.bx, wl.by, wl.scale)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[1], SMALL[3], SMALL[6]], ids=lambda w: w.name)
+def test_fwd(wl):
+    x = W.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] blocksparse_attn_fwd {wl.name}", flush=True)
+    o, lse = api().blocksparse_attn_fwd(g["q"], g["k"], g["v"], g["block_mask"], wl.bx, wl.by, wl.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.blocksparse_attention_forward(x["q"], x["k"], x["v"], x["block_mask"], wl.bx, wl.by, wl.scale)
+    check("o", o, ro, wl.dtype)
+    lg = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.all(np.abs(lg[fin] - rl[fin]) <= 1e-5 + 1e-5 * np.abs(rl[fin]))
+
+
+def test_ragged_config_full():
+    wl = W.WORKLOADS["ragged"]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv = gpu_bwd(wl, x)
+    ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
+                                                wl.bx, wl.by, wl.scale)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+def test_deterministic_and_fully_written():
+    wl = SMALL[6]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    g = {k: v.to(DEV) for k, v in x.items()}
+    a = api()
+    outs = []
+    for _ in range(3):
+        dq = torch.full_like(g["q"], float("nan"))
+        dk = torch.full_like(g["k"], float("nan"))
+        dv = torch.full_like(g["v"], float("nan"))
+        nbytes = a.blocksparse_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv, wl.bx, wl.by)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+        st = a.lib.blocksparse_attn_bwd(*(ctypes.c_void_p(t.data_ptr()) for t in (
+            g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["block_mask"], dq, dk, dv, ws)),
+            nbytes, wl.B, wl.Hq, wl.Sq, wl.Skv, 128, wl.bx, wl.by, wl.scale, a.MA_F16,
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv)])
+    for t in outs[0]:
+        assert torch.isfinite(t.float()).all()
+    for other in outs[1:]:
+        for u, v in zip(outs[0], other):
+            assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+@pytest.mark.slow
+def test_bigbird_config_sampled():
+    wl = W.WORKLOADS["bigbird"]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv = gpu_bwd(wl, x)
+    rng = np.random.default_rng(9)
+    S = wl.Sq
+    rows = [0, 1, 63, 64, 65, 127, 128, 4095, S - 65, S - 64, S - 1] + list(rng.integers(0, S, 10))
+    qs = [(0, int(n), int(i)) for i in rows for n in (0, 9, 15)]
+    ks = [(0, int(n), int(j)) for j in rows for n in (0, 9, 15)]
+    ref = oracle.blocksparse_attention_backward_sampled(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"],
+                                                        x["block_mask"], wl.bx, wl.by, wl.scale, qs, ks)
+    check("dq[sampled]", torch.stack([dq[b, n, i] for b, n, i in qs]), ref["dq"], wl.dtype)
+    check("dk[sampled]", torch.stack([dk[b, n, j] for b, n, j in ks]), ref["dk"], wl.dtype)
+    check("dv[sampled]", torch.stack([dv[b, n, j] for b, n, j in ks]), ref["dv"], wl.dtype)

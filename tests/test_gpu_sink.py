@@ -1,0 +1,181 @@
+"""GPU parity of the sink + sliding-window path against the fp64 oracle.
+
+Inputs come from the seeded generator; O and lse come from the oracle's forward (rounded
+to the activation dtype and to fp32), never from the GPU.  Every element of dQ, dK, dV,
+dsink (and Delta) must pass the gate in ``parity.py``.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_attention_backward_amd import workloads as W
+from parity import check, ATOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def api():
+    from masked_attention_backward_amd import api as a
+    return a
+
+
+def with_oracle_forward(wl, x):
+    o, lse = oracle.sink_attention_forward(x["q"], x["k"], x["v"], x["sink"], wl.window, wl.scale)
+    x["o"] = torch.from_numpy(o).to(wl.dtype)
+    x["lse"] = torch.from_numpy(lse).to(torch.float32)
+    return x
+
+
+def gpu_bwd(wl, x):
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] attn_sink_bwd {wl.name} B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} S{wl.Sq} W{wl.window} {wl.dtype}", flush=True)
+    out = api().attn_sink_bwd(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], wl.window, wl.scale,
+                              return_delta=True)
+    torch.cuda.synchronize()
+    return out
+
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    W.custom_sink("s192_causal", 1, 2, 2, 192, 192, torch.float16, seed_base=101),
+    W.custom_sink("s200_w17_bf16", 2, 4, 2, 200, 17, torch.bfloat16, seed_base=102),
+    W.custom_sink("s300_w1", 1, 8, 1, 300, 1, torch.float16, seed_base=103),
+    W.custom_sink("s64_wbig", 1, 2, 1, 64, 100000, torch.float16, seed_base=104),
+    W.custom_sink("s1", 1, 2, 1, 1, 1, torch.bfloat16, seed_base=105),
+    W.custom_sink("s520_w300_bf16", 1, 4, 4, 520, 300, torch.bfloat16, seed_base=106),
+    W.custom_sink("s77_w5", 3, 6, 3, 77, 5, torch.float16, seed_base=107),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_bwd_small(wl):
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("delta", delta, ref["delta"], wl.dtype)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+def test_bwd_no_sink_equals_causal():
+    """sink = -inf: dsink is exactly 0 and the rest matches the oracle (plain causal attention)."""
+    wl = W.custom_sink("nosink", 1, 4, 2, 160, 160, torch.float16, seed_base=110)
+    x = W.make_inputs(wl)
+    x["sink"] = torch.full((wl.Hq,), float("-inf"))
+    x = with_oracle_forward(wl, x)
+    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    assert torch.all(dsink.cpu() == 0)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+def test_bwd_paired_tiles():
+    """Wide window with enough heads that both kernels run tile p together with tile n-1-p."""
+    wl = W.custom_sink("paired", 4, 16, 16, 1024, 1024, torch.float16, seed_base=111)
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[2], SMALL[6], W.custom_sink("f_causal", 1, 4, 1, 333, 333,
+                                                                             torch.float16, seed_base=112)],
+                         ids=lambda w: w.name)
+def test_fwd(wl):
+    x = W.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] attn_sink_fwd {wl.name}", flush=True)
+    o, lse = api().attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sink_attention_forward(x["q"], x["k"], x["v"], x["sink"], wl.window, wl.scale)
+    check("o", o, ro, wl.dtype)
+    err = np.abs(lse.cpu().double().numpy() - rl)
+    assert np.all(err <= 1e-5 + 1e-5 * np.abs(rl)), err.max()
+
+
+def test_mid_config():
+    wl = W.WORKLOADS["mid"]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+def test_deterministic_and_fully_written():
+    """Three runs are bit-identical, and outputs pre-filled with 0xFF (NaN) are fully overwritten."""
+    wl = W.custom_sink("det", 2, 8, 2, 333, 100, torch.bfloat16, seed_base=113)
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    g = {k: v.to(DEV) for k, v in x.items()}
+    a = api()
+    outs = []
+    for _ in range(3):
+        dq = torch.full_like(g["q"], float("nan"))
+        dk = torch.full_like(g["k"], float("nan"))
+        dv = torch.full_like(g["v"], float("nan"))
+        dsink = torch.full((wl.Hq,), float("nan"), device=DEV)
+        nbytes = a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+        st = a.lib.attn_sink_bwd(*(ctypes.c_void_p(t.data_ptr()) for t in (
+            g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], dq, dk, dv, dsink, ws)),
+            nbytes, wl.B, wl.Hq, wl.Hkv, wl.Sq, 128, wl.window, wl.scale, a.MA_BF16,
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv, dsink)])
+    for t in outs[0]:
+        assert torch.isfinite(t.float()).all()
+    for other in outs[1:]:
+        for u, v in zip(outs[0], other):
+            assert torch.equal(u.view(torch.int16) if u.dtype != torch.float32 else u.view(torch.int32),
+                               v.view(torch.int16) if v.dtype != torch.float32 else v.view(torch.int32))
+
+
+@pytest.mark.slow
+def test_large_window128_full():
+    wl = W.WORKLOADS["large_w128"]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+@pytest.mark.slow
+def test_large_causal_sampled():
+    """Full-size full-causal run (the benchmarked launch); outputs checked at sampled rows."""
+    wl = W.WORKLOADS["large_causal"]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
+    rng = np.random.default_rng(7)
+    S = wl.Sq
+    rows = [0, 1, 63, 64, 127, 128, 4095, 4096, S - 129, S - 128, S - 1] + list(rng.integers(0, S, 10))
+    qs = [(0, int(h), int(i)) for i in rows for h in (0, 37, 63)]
+    ks = [(0, int(h), int(j)) for j in rows for h in (0, 5, 7)]
+    ref = oracle.sink_attention_backward_sampled(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"],
+                                                 wl.window, wl.scale, qs, ks)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq[sampled]", torch.stack([dq[b, h, i] for b, h, i in qs]), ref["dq"], wl.dtype)
+    check("dk[sampled]", torch.stack([dk[b, h, j] for b, h, j in ks]), ref["dk"], wl.dtype)
+    check("dv[sampled]", torch.stack([dv[b, h, j] for b, h, j in ks]), ref["dv"], wl.dtype)
