@@ -91,9 +91,12 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
                   int B, int Hq, int Hkv, int S, int D, int window, float scale,
                   int dtype, void* stream);
 
-/* Workspace bytes attn_sink_bwd needs (0 on invalid sizes).  Layout (offsets in bytes):
- *   0:                 Delta [B, Hq, S] fp32  (Delta_i = dO_i . O_i; readable after the call)
- *   align256(4*B*Hq*S): dsink partials [B, Hq, ceil(S/64)] fp32 */
+/* Workspace bytes attn_sink_bwd needs (0 on invalid sizes).  Layout (offsets in bytes),
+ * with Sp = 64*ceil(S/64) and R = align256(4*B*Hq*Sp):
+ *   0:   Delta [B, Hq, Sp] fp32  (Delta_i = dO_i . O_i; readable after the call; rows >= S
+ *        hold 0)
+ *   R:   lse * log2(e) [B, Hq, Sp] fp32 (rows >= S hold +inf)
+ *   2R:  dsink partials [B, Hq, ceil(S/64)] fp32 */
 size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
 /* ---------------------------------------------------------------------------------
@@ -138,8 +141,10 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
 
 /* Workspace bytes blocksparse_attn_bwd needs (0 on invalid sizes).  Layout, each
  * region starting at a 256-byte boundary, in this order:
- *   Delta [B, N, Sq] fp32, mask_t [B, N, nkb, nqb] u8, sel_q [B, N, nqb, nkb] i32,
- *   cnt_q [B, N, nqb] i32, sel_k [B, N, nkb, nqb] i32, cnt_k [B, N, nkb] i32. */
+ *   Delta [B, N, Sqp] fp32, lse * log2(e) [B, N, Sqp] fp32 (Sqp = 64*ceil(Sq/64)),
+ *   mask_t [B, N, nkb, nqb] u8,
+ *   sel_q [B, N, nqb, nkb] i32, cnt_q [B, N, nqb] i32, sel_k [B, N, nkb, nqb] i32,
+ *   cnt_k [B, N, nkb] i32. */
 size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by);
 
 /* ---------------------------------------------------------------------------------

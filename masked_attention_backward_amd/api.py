@@ -153,7 +153,8 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
                            _dtype_code(q), _stream(dev))
     _check("attn_sink_bwd", st)
     if return_delta:
-        delta = ws[: B * Hq * S * 4].view(torch.float32).view(B, Hq, S)
+        sp = (S + 63) // 64 * 64
+        delta = ws[: B * Hq * sp * 4].view(torch.float32).view(B, Hq, sp)[..., :S]
         return dq, dk, dv, dsink, delta
     return dq, dk, dv, dsink
 

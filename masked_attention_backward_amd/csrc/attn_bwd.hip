@@ -25,7 +25,9 @@
 namespace ma {
 
 // ------------------------------------------------------------------------ preprocess
-// Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]  (fp32), one 64-row block per workgroup.
+// Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]  (fp32) and lse2 = lse * log2(e), one
+// 64-row block per workgroup, into per-row buffers padded to a multiple of 64 rows: padding
+// rows get Delta = 0 and lse2 = +inf, so exp2(s - lse2) is exactly 0 there.
 // With a sink: part[b,h,blk] = sum_{i in blk} exp(sink_h - lse_i) * Delta_i, summed in a
 // fixed order (tree over the 64 rows).
 template <class T, bool SINK>
@@ -33,11 +35,17 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ sink, float* __restrict__ delta,
-                                                         float* __restrict__ part, int H, int S, int nblk) {
+                                                         float* __restrict__ lse2, float* __restrict__ part, int H,
+                                                         int S, int nblk) {
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, rsub = tid >> 4, ch = tid & 15;
   __shared__ float sd[64];
   const size_t head = ((size_t)b * H + h) * (size_t)S;
+  const size_t phead = ((size_t)b * H + h) * (size_t)nblk * 64;
+  if (tid < 64) {
+    const int row = blk * 64 + tid;
+    lse2[phead + row] = (row < S) ? lse[head + row] * LOG2E : INFINITY;
+  }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int row = blk * 64 + pass * 16 + rsub;
@@ -56,8 +64,8 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     acc += __shfl_xor(acc, 2, 16);
     acc += __shfl_xor(acc, 1, 16);
     if (ch == 0) {
-      if (row < S) delta[head + row] = acc;
-      sd[pass * 16 + rsub] = (row < S) ? acc : 0.f;
+      delta[phead + row] = acc;
+      sd[pass * 16 + rsub] = acc;
     }
   }
   if constexpr (SINK) {
@@ -118,40 +126,130 @@ struct BlockSource {
 
 // ----------------------------------------------------------------------- dK / dV
 // Workgroup = NW waves owning 32*NW consecutive key rows (wave w: rows c0+32w .. +32).
-// Per visited (head, query tile of 64 rows):
+// Per visited (query head, query tile of 64 rows), in two 32-row query blocks mb:
 //   S[q][kv]  = Q K^T          A = Q rows (LDS),   B = K rows (registers)
 //   dP[q][kv] = dO V^T         A = dO rows (LDS),  B = V rows (registers)
 //   P = exp2(S*scale*log2e - lse*log2e), dS = P (dP - Delta)   (accumulator layout:
 //       lane column = key row, registers = query rows)
 //   dV[kv][d] += P^T dO        A = P^T (repacked accumulator), B = dO columns (tr read)
 //   dK[kv][d] += dS^T Q        A = dS^T,                       B = Q columns (tr read)
+// The instruction stream of one tile is laid out by hand (sched_barrier between steps):
+//   steps 0-7:   S/dP of block 0
+//   steps 8-15:  S/dP of block 1, interleaved with the softmax of block 0 (4 chunks)
+//   steps 16-23: dV/dK of block 0, interleaved with the softmax of block 1 (4 chunks)
+//   steps 24-31: dV/dK of block 1
+// Operand fragments are loaded ahead of their MFMA, so LDS latency hides under the matrix
+// core while only a few fragments are live at once.
+template <class T, int NW>
+struct DkdvCtx {
+  u32x4 kf[8], vf[8];
+  f32x16 dk[4], dv[4];
+};
+
+// One quarter of a block's softmax: rows 8 g4 + 4 h + e (e = 0..3) of block mb; writes
+// k-slots 4 (g4 % 2) .. +3 of the P^T / dS^T operands of k-step g4 / 2 of the block.
+// `ld` points at this stage's lse2 row (64 floats) followed by its Delta row (64 floats).
+template <class T, int MASK, bool MASKED>
+__device__ __forceinline__ void dkdv_softmax_chunk(const f32x16& s, const f32x16& dp, u32x4* pa, u32x4* da,
+                                                   const float* ld, int mb, int g4, float sl2, int qdiff, int window,
+                                                   uint64_t hbits) {
+  const int qo = mb * 32 + 8 * g4;
+  const float4 L = *reinterpret_cast<const float4*>(ld + qo);
+  const float4 Dd = *reinterpret_cast<const float4*>(ld + 64 + qo);
+  const float Lv[4] = {L.x, L.y, L.z, L.w};
+  const float Dv[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
+  float p[4], ds[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g4 + e;
+    float v = fast_exp2(fmaf(s[r], sl2, -Lv[e]));
+    if constexpr (MASKED) {
+      bool vis;
+      if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(qdiff + qo + e) < (unsigned)window;
+      else vis = (hbits >> (qo + e)) & 1ull;
+      v = vis ? v : 0.f;
+    }
+    p[e] = v;
+    ds[e] = v * (dp[r] - Dv[e]);
+  }
+  pa[g4 >> 1][2 * (g4 & 1)] = T::pack2(p[0], p[1]);
+  pa[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(p[2], p[3]);
+  da[g4 >> 1][2 * (g4 & 1)] = T::pack2(ds[0], ds[1]);
+  da[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(ds[2], ds[3]);
+}
+
+// One tile: tile A of the stage = Q, tile B = dO.
+template <class T, int MASK, int NW, bool MASKED>
+__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const uint16_t* stages,
+                                             const float* ld, float sl2, int qdiff, int window, uint64_t hbits) {
+  f32x16 s0, d0, s1, d1;
+  u32x4 qa[2], oa[2];
+  qa[0] = frag_row(stages, fo, 0, 0, 0);
+  oa[0] = frag_row(stages, fo, 1, 0, 0);
+  qa[1] = frag_row(stages, fo, 0, 1, 0);
+  oa[1] = frag_row(stages, fo, 1, 1, 0);
+  u32x4 pa0[2], da0[2], pa1[2], da1[2];
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int mb = st >> 3, ks = st & 7;
+    f32x16& sc = mb ? s1 : s0;
+    f32x16& dc = mb ? d1 : d0;
+    sc = T::mma(qa[st & 1], x.kf[ks], ks ? sc : zero16());
+    dc = T::mma(oa[st & 1], x.vf[ks], ks ? dc : zero16());
+    if (st + 2 < 16) {
+      qa[st & 1] = frag_row(stages, fo, 0, (st + 2) & 7, (st + 2) >> 3);
+      oa[st & 1] = frag_row(stages, fo, 1, (st + 2) & 7, (st + 2) >> 3);
+    }
+    if (mb == 1 && (ks & 1) == 0)
+      dkdv_softmax_chunk<T, MASK, MASKED>(s0, d0, pa0, da0, ld, 0, ks >> 1, sl2, qdiff, window, hbits);
+    MA_STEP();
+  }
+  u32x4 bo[2], bq[2];
+  bo[0] = frag_col(stages, fo, 1, 0, 0);
+  bq[0] = frag_col(stages, fo, 0, 0, 0);
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int t4 = st >> 2, nb = st & 3;
+    if (st + 1 < 16) {
+      bo[(st + 1) & 1] = frag_col(stages, fo, 1, (st + 1) >> 2, (st + 1) & 3);
+      bq[(st + 1) & 1] = frag_col(stages, fo, 0, (st + 1) >> 2, (st + 1) & 3);
+    }
+    const u32x4& pa = t4 < 2 ? pa0[t4] : pa1[t4 - 2];
+    const u32x4& da = t4 < 2 ? da0[t4] : da1[t4 - 2];
+    x.dv[nb] = T::mma(pa, bo[st & 1], x.dv[nb]);
+    x.dk[nb] = T::mma(da, bq[st & 1], x.dk[nb]);
+    if (st < 8 && (st & 1) == 0)
+      dkdv_softmax_chunk<T, MASK, MASKED>(s1, d1, pa1, da1, ld, 1, st >> 1, sl2, qdiff, window, hbits);
+    MA_STEP();
+  }
+}
+
 template <class T, int MASK, int NW>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kb,
-                                          uint16_t (*sQ)[TILE_ELEMS], uint16_t (*sO)[TILE_ELEMS],
-                                          float (*sL)[64], float (*sD)[64]) {
-  constexpr int NT = NW * 64;
+                                          uint16_t* stages, float* sld) {
   constexpr int BC = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const size_t kvhead = (size_t)b * a.Hkv + kvh;
   const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
   const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
 
+  DkdvCtx<T, NW> x;
   // This lane's key row (clamped into the sequence; rows past the end are never stored).
   const int kr = min(c0 + 32 * w + c, a.Skv - 1);
-  u32x4 kf[8], vf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    kf[ks] = ld16(Kp + (size_t)kr * HD + ks * 16 + 8 * h);
-    vf[ks] = ld16(Vp + (size_t)kr * HD + ks * 16 + 8 * h);
+    x.kf[ks] = ld16(Kp + (size_t)kr * HD + ks * 16 + 8 * h);
+    x.vf[ks] = ld16(Vp + (size_t)kr * HD + ks * 16 + 8 * h);
   }
-  f32x16 dk[4], dv[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    dk[nb] = zero16();
-    dv[nb] = zero16();
+    x.dk[nb] = zero16();
+    x.dv[nb] = zero16();
   }
 
-  // Visit order.
   WindowSource wsrc{};
   BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
   if constexpr (MASK == MASK_WINDOW) {
@@ -167,102 +265,50 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
     else return bsrc.next(hd, t, bits);
   };
-
-  TileStage<NT> stq, sto;
-  constexpr int LPT = (128 + NT - 1) / NT;
-  float stl[LPT];
-  auto load = [&](int hd, int t) {
+  // Prefetch tile (hd, t) into stage `stg`: Q -> tile A, dO -> tile B, lse2/Delta rows.
+  auto issue = [&](int hd, int t, int stg) {
     const size_t qhead = (size_t)b * a.Hq + hd;
-    const uint16_t* Qp = (const uint16_t*)a.q + qhead * a.Sq * HD;
-    const uint16_t* Op = (const uint16_t*)a.dout + qhead * a.Sq * HD;
-    stq.load(Qp, t * 64, a.Sq, tid);
-    sto.load(Op, t * 64, a.Sq, tid);
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < 128) {
-        const int row = min(t * 64 + (idx & 63), a.Sq - 1);
-        stl[i] = (idx < 64) ? a.lse[qhead * a.Sq + row] * LOG2E : a.delta[qhead * a.Sq + row];
-      }
-    }
+    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
+    tile_load_async<NW>(dst, (const uint16_t*)a.q + qhead * a.Sq * HD, t * 64, a.Sq, w, lane);
+    tile_load_async<NW>(dst + TILE_ELEMS, (const uint16_t*)a.dout + qhead * a.Sq * HD, t * 64, a.Sq, w, lane);
+    if (w == 0) row_load_async(sld + stg * 128, a.lse2 + qhead * sq_pad + t * 64, lane);
+    if (w == NW - 1) row_load_async(sld + stg * 128 + 64, a.delta + qhead * sq_pad + t * 64, lane);
   };
 
+  const float sl2 = a.scale_log2;
+  const int kj = c0 + 32 * w + c;
+  FragOff fo(lane);
+  int stage = 0;
   int hn = 0, tn = 0;
   uint64_t bn = 0;
-  bool have = next(hn, tn, bn);
-  if (have) load(hn, tn);
-  int buf = 0;
-  const float sl2 = a.scale_log2;
-  const WindowVis wv{a.Sq, a.Skv, a.window};
-  while (have) {
+  // Window tiles that need no mask: every (q, kv) of the pair lies inside the window.
+  // Rows past the sequence end need none either (lse2 = +inf there), nor do key columns
+  // past the end (never stored).
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (tn * 64 - (c0 + BC - 1) >= 0) && (tn * 64 + 63 - c0 < a.window);
+    else
+      return bn == ~0ull;
+  };
+  auto step = [&](auto masked) -> bool {
+    constexpr bool MASKED = decltype(masked)::value;
     const int t = tn;
     const uint64_t bits = bn;
-    stq.store(sQ[buf], tid);
-    sto.store(sO[buf], tid);
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < 64) sL[buf][idx] = stl[i];
-      else if (idx < 128) sD[buf][idx - 64] = stl[i];
-    }
+    wait_async_loads();
     __syncthreads();
-    have = next(hn, tn, bn);
-    if (have) load(hn, tn);
+    const bool more = next(hn, tn, bn);
+    if (more) issue(hn, tn, stage ^ 1);
+    const int qdiff = t * 64 + 4 * h - kj;
+    const uint64_t hbits = h ? (bits >> 4) : bits;
+    dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + stage * 128 + 4 * h, sl2, qdiff, a.window, hbits);
+    fo.flip();
+    stage ^= 1;
+    return more;
+  };
 
-    const uint16_t* tq = sQ[buf];
-    const uint16_t* to = sO[buf];
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = zero16();
-      dp[mb] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s[mb] = T::mma(frag_row(tq, mb * 32 + c, ks, h), kf[ks], s[mb]);
-        dp[mb] = T::mma(frag_row(to, mb * 32 + c, ks, h), vf[ks], dp[mb]);
-      }
-    }
-    const int q0 = t * 64;
-    bool full;
-    if constexpr (MASK == MASK_WINDOW) full = wv.full(q0, 64, c0, BC);
-    else full = (bits == ~0ull);
-    const int kj = c0 + 32 * w + c;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qo = mb * 32 + 8 * g4 + 4 * h;
-        const float4 L = *reinterpret_cast<const float4*>(&sL[buf][qo]);
-        const float4 Dd = *reinterpret_cast<const float4*>(&sD[buf][qo]);
-        const float Lv[4] = {L.x, L.y, L.z, L.w};
-        const float Dv[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float p = fast_exp2(s[mb][r] * sl2 - Lv[e]);
-          if (!full) {
-            bool vis;
-            if constexpr (MASK == MASK_WINDOW) vis = wv.vis(q0 + qo + e, kj);
-            else vis = (bits >> (qo + e)) & 1ull;
-            p = vis ? p : 0.f;
-          }
-          s[mb][r] = p;
-          dp[mb][r] = p * (dp[mb][r] - Dv[e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4 pa = pack8<T>(s[t4 >> 1], 8 * (t4 & 1));
-      const u32x4 da = pack8<T>(dp[t4 >> 1], 8 * (t4 & 1));
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        dv[nb] = T::mma(pa, frag_col(to, t4, nb * 32, lane), dv[nb]);
-        dk[nb] = T::mma(da, frag_col(tq, t4, nb * 32, lane), dk[nb]);
-      }
-    }
-    buf ^= 1;
-  }
+  bool have = next(hn, tn, bn);
+  if (have) issue(hn, tn, 0);
+  run_tiles(have, step, is_full);
 
   // Epilogue: rows c0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
@@ -273,8 +319,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     for (int r = 0; r < 16; ++r) {
       const int row = c0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
       if (row < kv_end) {
-        dKp[(size_t)row * HD + nb * 32 + c] = T::one(dk[nb][r] * a.scale);
-        dVp[(size_t)row * HD + nb * 32 + c] = T::one(dv[nb][r]);
+        dKp[(size_t)row * HD + nb * 32 + c] = T::one(x.dk[nb][r] * a.scale);
+        dVp[(size_t)row * HD + nb * 32 + c] = T::one(x.dv[nb][r]);
       }
     }
   }
@@ -282,39 +328,103 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sD[2][64];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float sld[2 * 128];
   const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BC = 32 * NW;
-    dkdv_tile<T, MASK, NW>(a, b, kvh, p * BC, a.Skv, 0, sQ, sO, sL, sD);
+    dkdv_tile<T, MASK, NW>(a, b, kvh, p * BC, a.Skv, 0, stages, sld);
     const int p2 = a.n_tiles - 1 - p;
     if (a.pair && p2 != p) {
       __syncthreads();
-      dkdv_tile<T, MASK, NW>(a, b, kvh, p2 * BC, a.Skv, 0, sQ, sO, sL, sD);
+      dkdv_tile<T, MASK, NW>(a, b, kvh, p2 * BC, a.Skv, 0, stages, sld);
     }
   } else {
     const int c0 = p * a.by;
-    dkdv_tile<T, MASK, NW>(a, b, kvh, c0, min(c0 + a.by, a.Skv), p, sQ, sO, sL, sD);
+    dkdv_tile<T, MASK, NW>(a, b, kvh, c0, min(c0 + a.by, a.Skv), p, stages, sld);
   }
 }
 
 // --------------------------------------------------------------------------- dQ
 // Workgroup = NW waves owning 32*NW consecutive query rows (wave w: rows r0+32w .. +32).
-// Per visited key tile of 64 rows:
+// Per visited key tile of 64 rows, in two 32-row key blocks mb:
 //   S^T[kv][q]  = K Q^T       A = K rows (LDS),  B = Q rows (registers)
 //   dP^T[kv][q] = V dO^T      A = V rows (LDS),  B = dO rows (registers)
 //   (accumulator layout: lane column = query row, registers = key rows)
 //   dQ[q][d] += dS K          A = dS (repacked accumulator), B = K columns (tr read)
+// Hand-laid stream as in dK/dV: S/dP of block 0; S/dP of block 1 + softmax of block 0;
+// dQ of block 0 + softmax of block 1; dQ of block 1.
+template <class T, int MASK, bool MASKED>
+__device__ __forceinline__ void dq_softmax_chunk(const f32x16& s, const f32x16& dp, u32x4* da, int mb, int g4,
+                                                 float sl2, float l2, float dd, int kdiff, int window,
+                                                 uint64_t hbits) {
+  float ds[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g4 + e;
+    const int ko = mb * 32 + 8 * g4 + e;
+    float v = fast_exp2(fmaf(s[r], sl2, -l2));
+    if constexpr (MASKED) {
+      bool vis;
+      if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
+      else vis = (hbits >> ko) & 1ull;
+      v = vis ? v : 0.f;
+    }
+    ds[e] = v * (dp[r] - dd);
+  }
+  da[g4 >> 1][2 * (g4 & 1)] = T::pack2(ds[0], ds[1]);
+  da[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(ds[2], ds[3]);
+}
+
+// One key tile: tile A of the stage = K, tile B = V.
+template <class T, int MASK, bool MASKED>
+__device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
+                                           const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
+                                           int window, uint64_t hbits) {
+  f32x16 s0, d0, s1, d1;
+  u32x4 ka[2], va[2];
+  ka[0] = frag_row(stages, fo, 0, 0, 0);
+  va[0] = frag_row(stages, fo, 1, 0, 0);
+  ka[1] = frag_row(stages, fo, 0, 1, 0);
+  va[1] = frag_row(stages, fo, 1, 1, 0);
+  u32x4 da0[2], da1[2];
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int mb = st >> 3, ks = st & 7;
+    f32x16& sc = mb ? s1 : s0;
+    f32x16& dc = mb ? d1 : d0;
+    sc = T::mma(ka[st & 1], qf[ks], ks ? sc : zero16());
+    dc = T::mma(va[st & 1], of[ks], ks ? dc : zero16());
+    if (st + 2 < 16) {
+      ka[st & 1] = frag_row(stages, fo, 0, (st + 2) & 7, (st + 2) >> 3);
+      va[st & 1] = frag_row(stages, fo, 1, (st + 2) & 7, (st + 2) >> 3);
+    }
+    if (mb == 1 && (ks & 1) == 0)
+      dq_softmax_chunk<T, MASK, MASKED>(s0, d0, da0, 0, ks >> 1, sl2, l2, dd, kdiff, window, hbits);
+    MA_STEP();
+  }
+  u32x4 bk[2];
+  bk[0] = frag_col(stages, fo, 0, 0, 0);
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int t4 = st >> 2, nb = st & 3;
+    if (st + 1 < 16) bk[(st + 1) & 1] = frag_col(stages, fo, 0, (st + 1) >> 2, (st + 1) & 3);
+    const u32x4& da = t4 < 2 ? da0[t4] : da1[t4 - 2];
+    acc[nb] = T::mma(da, bk[st & 1], acc[nb]);
+    if (st < 8 && (st & 1) == 0)
+      dq_softmax_chunk<T, MASK, MASKED>(s1, d1, da1, 1, st >> 1, sl2, l2, dd, kdiff, window, hbits);
+    MA_STEP();
+  }
+}
+
 template <class T, int MASK, int NW>
 __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
-                                        uint16_t (*sK)[TILE_ELEMS], uint16_t (*sV)[TILE_ELEMS]) {
-  constexpr int NT = NW * 64;
+                                        uint16_t* stages) {
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const size_t qhead = (size_t)b * a.Hq + hq;
@@ -322,6 +432,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   const size_t kvhead = (size_t)b * a.Hkv + kvh;
   const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
   const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
 
   const int qi = r0 + 32 * w + c;
   const int qr = min(qi, a.Sq - 1);
@@ -333,8 +444,8 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     qf[ks] = ld16(Qp + ks * 16 + 8 * h);
     of[ks] = ld16(Op + ks * 16 + 8 * h);
   }
-  const float l2 = a.lse[qhead * a.Sq + qr] * LOG2E;
-  const float dd = a.delta[qhead * a.Sq + qr];
+  const float l2 = a.lse2[qhead * sq_pad + qr];
+  const float dd = a.delta[qhead * sq_pad + qr];
   f32x16 acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
@@ -354,69 +465,45 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
     else return bsrc.next(hd, t, bits);
   };
+  auto issue = [&](int t, int stg) {
+    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
+    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, w, lane);
+    tile_load_async<NW>(dst + TILE_ELEMS, Vp, t * 64, a.Skv, w, lane);
+  };
 
-  TileStage<NT> stk, stv;
+  const float sl2 = a.scale_log2;
+  FragOff fo(lane);
+  int stage = 0;
   int hn = 0, tn = 0;
   uint64_t bn = 0;
-  bool have = next(hn, tn, bn);
-  if (have) {
-    stk.load(Kp, tn * 64, a.Skv, tid);
-    stv.load(Vp, tn * 64, a.Skv, tid);
-  }
-  int buf = 0;
-  const float sl2 = a.scale_log2;
-  const WindowVis wv{a.Sq, a.Skv, a.window};
-  while (have) {
+  // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
+  // workgroup (query rows past the end are never stored; key rows past the end always
+  // fail the window test since Sq == Skv on the window path).
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (r0 - (tn * 64 + 63) >= 0) && (r0 + BQ - 1 - tn * 64 < a.window);
+    else
+      return bn == ~0ull;
+  };
+  auto step = [&](auto masked) -> bool {
+    constexpr bool MASKED = decltype(masked)::value;
     const int t = tn;
     const uint64_t bits = bn;
-    stk.store(sK[buf], tid);
-    stv.store(sV[buf], tid);
+    wait_async_loads();
     __syncthreads();
-    have = next(hn, tn, bn);
-    if (have) {
-      stk.load(Kp, tn * 64, a.Skv, tid);
-      stv.load(Vp, tn * 64, a.Skv, tid);
-    }
-    const uint16_t* tk = sK[buf];
-    const uint16_t* tv = sV[buf];
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = zero16();
-      dp[mb] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s[mb] = T::mma(frag_row(tk, mb * 32 + c, ks, h), qf[ks], s[mb]);
-        dp[mb] = T::mma(frag_row(tv, mb * 32 + c, ks, h), of[ks], dp[mb]);
-      }
-    }
-    const int k0 = t * 64;
-    bool full;
-    if constexpr (MASK == MASK_WINDOW) full = wv.full(r0, BQ, k0, 64);
-    else full = (bits == ~0ull);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ko = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float p = fast_exp2(s[mb][r] * sl2 - l2);
-        if (!full) {
-          bool vis;
-          if constexpr (MASK == MASK_WINDOW) vis = wv.vis(qi, k0 + ko);
-          else vis = (bits >> ko) & 1ull;
-          p = vis ? p : 0.f;
-        }
-        dp[mb][r] = p * (dp[mb][r] - dd);
-      }
-    }
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4 da = pack8<T>(dp[t4 >> 1], 8 * (t4 & 1));
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(da, frag_col(tk, t4, nb * 32, lane), acc[nb]);
-    }
-    buf ^= 1;
-  }
+    const bool more = next(hn, tn, bn);
+    if (more) issue(tn, stage ^ 1);
+    const int kdiff = qi - t * 64 - 4 * h;
+    const uint64_t hbits = h ? (bits >> 4) : bits;
+    dq_compute<T, MASK, MASKED>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits);
+    fo.flip();
+    stage ^= 1;
+    return more;
+  };
+
+  bool have = next(hn, tn, bn);
+  if (have) issue(tn, 0);
+  run_tiles(have, step, is_full);
 
   // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
@@ -432,8 +519,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
   const int nbh = a.B * a.Hq;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
@@ -442,37 +528,37 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
     constexpr int BQ = 32 * NW;
     // Heaviest query tiles (most visible keys) are dispatched first.
     const int t1 = a.n_tiles - 1 - p;
-    dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, sK, sV);
+    dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
     const int t2 = p;
     if (a.pair && t2 != t1) {
       __syncthreads();
-      dq_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, sK, sV);
+      dq_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, stages);
     }
   } else {
     const int r0 = p * a.bx;
-    dq_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, sK, sV);
+    dq_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
   }
 }
 
 // ------------------------------------------------------------------------ launchers
 template <class T>
 static hipError_t launch_preprocess_t(const void* o, const void* dout, const float* lse, const float* sink,
-                                      float* delta, float* part, int B, int H, int S, hipStream_t st) {
-  const int nblk = (S + 63) / 64;
+                                      float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st) {
+  const int nblk = (S + 63) / 64;   // Delta / lse2 rows are padded to nblk * 64
   dim3 grid(nblk, H, B);
   if (sink)
     hipLaunchKernelGGL((preprocess_kernel<T, true>), grid, dim3(256), 0, st, (const uint16_t*)o,
-                       (const uint16_t*)dout, lse, sink, delta, part, H, S, nblk);
+                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk);
   else
     hipLaunchKernelGGL((preprocess_kernel<T, false>), grid, dim3(256), 0, st, (const uint16_t*)o,
-                       (const uint16_t*)dout, lse, sink, delta, part, H, S, nblk);
+                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk);
   return hipGetLastError();
 }
 
 hipError_t launch_preprocess(int dtype, const void* o, const void* dout, const float* lse, const float* sink,
-                             float* delta, float* part, int B, int H, int S, hipStream_t st) {
-  return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, part, B, H, S, st)
-                    : launch_preprocess_t<F16>(o, dout, lse, sink, delta, part, B, H, S, st);
+                             float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st) {
+  return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st)
+                    : launch_preprocess_t<F16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st);
 }
 
 hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, int S, hipStream_t st) {

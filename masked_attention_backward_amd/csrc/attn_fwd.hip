@@ -20,8 +20,7 @@ namespace ma {
 
 template <class T, int MASK, int NW>
 __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
-                                         uint16_t (*sK)[TILE_ELEMS], uint16_t (*sV)[TILE_ELEMS]) {
-  constexpr int NT = NW * 64;
+                                         uint16_t* stages) {
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const size_t qhead = (size_t)b * a.Hq + hq;
@@ -73,54 +72,52 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
       return walk.next(t, bits);
     }
   };
+  auto issue = [&](int t, int stg) {
+    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
+    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, w, lane);
+    tile_load_async<NW>(dst + TILE_ELEMS, Vp, t * 64, a.Skv, w, lane);
+  };
 
-  TileStage<NT> stk, stv;
+  const float sl2 = a.scale_log2;
+  FragOff fo(lane);
+  int stage = 0;
   int tn = 0;
   uint64_t bn = 0;
-  bool have = next(tn, bn);
-  if (have) {
-    stk.load(Kp, tn * 64, a.Skv, tid);
-    stv.load(Vp, tn * 64, a.Skv, tid);
-  }
-  int buf = 0;
-  const float sl2 = a.scale_log2;
-  const WindowVis wv{a.Sq, a.Skv, a.window};
-  while (have) {
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (r0 - (tn * 64 + 63) >= 0) && (r0 + BQ - 1 - tn * 64 < a.window);
+    else
+      return bn == ~0ull;
+  };
+  auto step = [&](auto masked) -> bool {
+    constexpr bool MASKED = decltype(masked)::value;
     const int t = tn;
     const uint64_t bits = bn;
-    stk.store(sK[buf], tid);
-    stv.store(sV[buf], tid);
+    wait_async_loads();
     __syncthreads();
-    have = next(tn, bn);
-    if (have) {
-      stk.load(Kp, tn * 64, a.Skv, tid);
-      stv.load(Vp, tn * 64, a.Skv, tid);
-    }
-    const uint16_t* tk = sK[buf];
-    const uint16_t* tv = sV[buf];
+    const bool more = next(tn, bn);
+    if (more) issue(tn, stage ^ 1);
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = zero16();
+      s[mb] = T::mma(frag_row(stages, fo, 0, 0, mb), qf[0], zero16());
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[mb] = T::mma(frag_row(tk, mb * 32 + c, ks, h), qf[ks], s[mb]);
+      for (int ks = 1; ks < 8; ++ks) s[mb] = T::mma(frag_row(stages, fo, 0, ks, mb), qf[ks], s[mb]);
     }
-    const int k0 = t * 64;
-    bool full;
-    if constexpr (MASK == MASK_WINDOW) full = wv.full(r0, BQ, k0, 64);
-    else full = (bits == ~0ull);
+    const int kdiff = qi - t * 64 - 4 * h;
+    const uint64_t hbits = h ? (bits >> 4) : bits;
     // Scaled logits in the log2 domain; hidden entries become -inf.
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ko = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int ko = mb * 32 + 8 * (r >> 2) + (r & 3);
         float x = s[mb][r] * sl2;
-        if (!full) {
+        if constexpr (MASKED) {
           bool vis;
-          if constexpr (MASK == MASK_WINDOW) vis = wv.vis(qi, k0 + ko);
-          else vis = (bits >> ko) & 1ull;
+          if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)a.window;
+          else vis = (hbits >> ko) & 1ull;
           x = vis ? x : -INFINITY;
         }
         s[mb][r] = x;
@@ -152,10 +149,16 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     for (int t4 = 0; t4 < 4; ++t4) {
       const u32x4 pb = pack8<T>(s[t4 >> 1], 8 * (t4 & 1));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(frag_col(tv, t4, nb * 32, lane), pb, acc[nb]);
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(frag_col(stages, fo, 1, t4, nb), pb, acc[nb]);
     }
-    buf ^= 1;
-  }
+    fo.flip();
+    stage ^= 1;
+    return more;
+  };
+
+  bool have = next(tn, bn);
+  if (have) issue(tn, 0);
+  run_tiles(have, step, is_full);
 
   // Epilogue: lane (c, h) holds O^T[d = nb*32 + 8(r/4) + 4h + r%4][q = qi].
   if (qi < q_end) {
@@ -177,8 +180,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
   const int nbh = a.B * a.Hq;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
@@ -186,10 +188,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BQ = 32 * NW;
     const int t1 = a.n_tiles - 1 - p;
-    fwd_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, sK, sV);
+    fwd_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
   } else {
     const int r0 = p * a.bx;
-    fwd_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, sK, sV);
+    fwd_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
   }
 }
 

@@ -18,6 +18,9 @@ constexpr int kMaxDim = 65535;    // grid y/z limits of the preprocess launch
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Per-row fp32 buffers (Delta, lse * log2 e) are padded to a multiple of 64 rows per head.
+size_t pad64(int S) { return ((size_t)S + 63) & ~(size_t)63; }
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
@@ -45,14 +48,15 @@ int check_blocks(int bx, int by) {
 }
 
 struct BlockLayout {
-  size_t delta, mask_t, sel_q, cnt_q, sel_k, cnt_k, total;
+  size_t delta, lse2, mask_t, sel_q, cnt_q, sel_k, cnt_k, total;
 };
 
 BlockLayout block_layout(int B, int N, int Sq, int nqb, int nkb) {
   BlockLayout l;
   const size_t bn = (size_t)B * N;
   l.delta = 0;
-  l.mask_t = align256(l.delta + bn * Sq * sizeof(float));
+  l.lse2 = align256(l.delta + bn * pad64(Sq) * sizeof(float));
+  l.mask_t = align256(l.lse2 + bn * pad64(Sq) * sizeof(float));
   l.sel_q = align256(l.mask_t + bn * nkb * nqb);
   l.cnt_q = align256(l.sel_q + bn * nqb * nkb * sizeof(int32_t));
   l.sel_k = align256(l.cnt_q + bn * nqb * sizeof(int32_t));
@@ -117,9 +121,9 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
 
 size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
   if (check_common(B, Hq, Hkv, S, D, 1.f, MA_F16) != MA_OK) return 0;
-  const size_t rows = (size_t)B * Hq * S;
+  const size_t rows = align256((size_t)B * Hq * pad64(S) * sizeof(float));
   const size_t nblk = (size_t)B * Hq * ((S + 63) / 64);
-  return align256(align256(rows * sizeof(float)) + nblk * sizeof(float));
+  return align256(2 * rows + nblk * sizeof(float));
 }
 
 static int sink_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -137,11 +141,13 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   const size_t need = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D);
   if (workspace_bytes < need) return MA_EWORKSPACE;
   hipStream_t hs = (hipStream_t)stream;
+  const size_t rows = align256((size_t)B * Hq * pad64(S) * sizeof(float));
   float* delta = at<float>(workspace, 0);
-  float* part = at<float>(workspace, align256((size_t)B * Hq * S * sizeof(float)));
+  float* lse2 = at<float>(workspace, rows);
+  float* part = at<float>(workspace, 2 * rows);
 
   if (events) hipEventRecord((hipEvent_t)events[0], hs);
-  hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, part, B, Hq, S, hs);
+  hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, lse2, part, B, Hq, S, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
   e = ma::launch_dsink_reduce(part, dsink, B, Hq, S, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
@@ -149,6 +155,7 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   AttnArgs a = base_args(q, k, v, B, Hq, Hkv, S, S, scale);
   a.dout = dout;
   a.lse = lse;
+  a.lse2 = lse2;
   a.delta = delta;
   a.sink = sink;
   a.dq = dq;
@@ -255,12 +262,14 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
                                         at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), hs);
   if (e != hipSuccess) return MA_ELAUNCH;
   float* delta = at<float>(workspace, L.delta);
-  e = ma::launch_preprocess(dtype, o, dout, lse, nullptr, delta, nullptr, B, N, Sq, hs);
+  float* lse2 = at<float>(workspace, L.lse2);
+  e = ma::launch_preprocess(dtype, o, dout, lse, nullptr, delta, lse2, nullptr, B, N, Sq, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
   if (events) hipEventRecord((hipEvent_t)events[1], hs);
   AttnArgs a = base_args(q, k, v, B, N, N, Sq, Skv, scale);
   a.dout = dout;
   a.lse = lse;
+  a.lse2 = lse2;
   a.delta = delta;
   a.dq = dq;
   a.dk = dk;

@@ -25,6 +25,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Element-type traits: 16-bit storage, fp32 compute.
 struct F16 {
@@ -32,9 +35,9 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                   0, 0, 0);
   }
+  // Two fp32 values -> two halves, round to nearest even (one v_cvt_pk_f16_f32).
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
   }
   static __device__ __forceinline__ float lo(uint32_t x) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
@@ -50,9 +53,9 @@ struct BF16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
   }
+  // Two fp32 values -> two bfloat16, round to nearest even (one v_cvt_pk_bf16_f32).
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   }
   static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
   static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -137,6 +140,7 @@ struct AttnArgs {
   const void* o;
   const void* dout;
   const float* lse;
+  const float* lse2;     // lse * log2(e), written by the preprocess kernel
   const float* delta;
   const float* sink;
   void* dq;

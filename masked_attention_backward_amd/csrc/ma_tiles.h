@@ -10,6 +10,8 @@
 //     its 4 rows over 4 distinct 16-byte groups (MFMA operands taken down a column).
 #pragma once
 
+#include <type_traits>
+
 #include "ma_device.h"
 
 namespace ma {
@@ -24,26 +26,60 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// MFMA operand taken along a row: lane (c, h) gets columns [16*ks + 8*h, +8) of row `row`.
-__device__ __forceinline__ u32x4 frag_row(const uint16_t* tile, int row, int ks, int h) {
-  return ld16(tile + row * HD + (((2 * ks + h) ^ swz(row)) << 3));
+// Staged operand tiles live in one LDS array of two stages x two tiles (A, B): tile k of
+// stage s starts at byte (2 s + k) * 16384, so switching stage is one XOR of bit 15 in the
+// lane's offsets.
+constexpr int TILE_BYTES = TILE_ELEMS * 2;     // 16384
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // 32768
+
+// Lane-dependent byte offsets of the MFMA operand fragments inside the staged tiles, with
+// the current stage folded in.  Every fragment read is one of these offsets plus a
+// compile-time constant (the array's LDS base, 16384 B for tile B, 8192 B per 32-row block,
+// 4096 B per 16-row k-step), which the LDS instructions take as an immediate.
+//   row[ks]        operand taken along a row: lane (c, h) reads columns [16 ks + 8 h, +8)
+//                  of row c (add 8192 B for rows 32..63)
+//   col[2 nb + i]  operand taken down a column with ds_read_b64_tr_b16: lane l = 32 h + c
+//                  receives tile[row][32 nb + c] for the rows 16 t4 + 8 (s/4) + 4 h + (s%4),
+//                  s = 0..7 (i = s/4; add 4096 B per t4), i.e. the k-slot order an
+//                  accumulator tile has when it is fed back as an operand (accumulator
+//                  register r = 8 (t4%2) + s of row block t4/2)
+struct FragOff {
+  int row[8];
+  int col[8];
+  __device__ __forceinline__ explicit FragOff(int lane) {
+    const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) row[ks] = 2 * (c * HD + (((2 * ks + h) ^ swz(c)) << 3));
+    const int rin = (lane & 15) >> 2;
+    const int cs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      col[2 * nb] = 2 * tile_off(4 * h + rin, 32 * nb + cs);
+      col[2 * nb + 1] = 2 * tile_off(8 + 4 * h + rin, 32 * nb + cs);
+    }
+  }
+  // Switch to the other stage.
+  __device__ __forceinline__ void flip() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      row[i] ^= STAGE_BYTES;
+      col[i] ^= STAGE_BYTES;
+    }
+  }
+};
+
+// Row-taken fragment of tile k (0 = A, 1 = B) of the current stage.
+__device__ __forceinline__ u32x4 frag_row(const uint16_t* stages, const FragOff& f, int k, int ks, int mb) {
+  return ld16(reinterpret_cast<const char*>(stages) + f.row[ks] + k * TILE_BYTES + mb * 8192);
 }
 
-// MFMA operand taken down a column with the transposing LDS read.  Lane l = 32*h + c
-// receives the eight values tile[row][col0 + c] for the rows
-//     16*t4 + 8*(s/4) + 4*h + (s%4),   s = 0..7,
-// i.e. the k-slot order an accumulator tile has when it is fed back as an operand
-// (accumulator register r = 8*(t4%2) + s of row block t4/2).
-__device__ __forceinline__ u32x4 frag_col(const uint16_t* tile, int t4, int col0, int lane) {
-  const int h = lane >> 5;
-  const int rin = (lane & 15) >> 2;
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int r1 = 16 * t4 + 4 * h + rin;
-  const int r2 = r1 + 8;
+// Column-taken (transposing) fragment of tile k of the current stage.
+__device__ __forceinline__ u32x4 frag_col(const uint16_t* stages, const FragOff& f, int k, int t4, int nb) {
   typedef short short4v __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) short4v* lds_ptr;
-  short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(tile + tile_off(r1, col)));
-  short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(tile + tile_off(r2, col)));
+  const char* base = reinterpret_cast<const char*>(stages) + k * TILE_BYTES + t4 * 4096;
+  short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(base + f.col[2 * nb]));
+  short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(base + f.col[2 * nb + 1]));
   u32x2 xa = __builtin_bit_cast(u32x2, x);
   u32x2 ya = __builtin_bit_cast(u32x2, y);
   u32x4 o;
@@ -54,34 +90,38 @@ __device__ __forceinline__ u32x4 frag_col(const uint16_t* tile, int t4, int col0
   return o;
 }
 
-// Cooperative copy of one 64 x 128 tile from global memory (rows clamped into
-// [0, nrows), row stride HD) into registers, then into a swizzled LDS tile.
-template <int NT>
-struct TileStage {
-  static constexpr int CPT = (TILE_ROWS * 16 + NT - 1) / NT;   // 16-byte chunks per thread
-  u32x4 r[CPT];
-  __device__ __forceinline__ void load(const uint16_t* base, int row0, int nrows, int tid) {
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Cooperative load of one 64 x 128 tile (rows clamped into [0, nrows), row stride HD)
+// straight from global memory into a swizzled LDS tile (global_load_lds_dwordx4: each
+// wave-instruction fills 1 KiB = 4 rows of LDS, lane i writing bytes [16 i, 16 i + 16) of
+// it).  The swizzle is applied on the global side: the lane that fills physical chunk p
+// of row r fetches logical chunk p ^ f(r).  16 wave-instructions per tile, spread over
+// the NW waves of the workgroup.
+template <int NW>
+__device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* base, int row0, int nrows, int w,
+                                                int lane) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      if (CPT * NT == TILE_ROWS * 16 || idx < TILE_ROWS * 16) {
-        const int row = idx >> 4, ch = idx & 15;
-        const int g = min(row0 + row, nrows - 1);
-        r[i] = ld16(base + (size_t)g * HD + ch * 8);
-      }
+  for (int j = 0; j < (16 + NW - 1) / NW; ++j) {
+    const int u = w + j * NW;
+    if ((16 % NW) == 0 || u < 16) {
+      const int row = 4 * u + (lane >> 4);
+      const int p = lane & 15;
+      const int g = min(row0 + row, nrows - 1);
+      const uint16_t* src = base + (size_t)g * HD + ((p ^ swz(row)) << 3);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tile + u * 512), 16, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      if (CPT * NT == TILE_ROWS * 16 || idx < TILE_ROWS * 16) {
-        const int row = idx >> 4, ch = idx & 15;
-        st16(tile + row * HD + ((ch ^ swz(row)) << 3), r[i]);
-      }
-    }
-  }
-};
+}
+
+// 64 consecutive fp32 values straight into LDS by one wave (the per-row buffers are
+// padded to a multiple of 64 rows).
+__device__ __forceinline__ void row_load_async(float* dst, const float* src, int lane) {
+  __builtin_amdgcn_global_load_lds(src + lane, (lds_void_ptr)dst, 4, 0, 0);
+}
+
+// Wait for this wave's outstanding global->LDS loads.
+__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Visibility of the elements of one (query-tile, key-tile) pair.
 //   window:  query i sees key j iff 0 <= i - j < window, both inside their sequences
@@ -96,5 +136,25 @@ struct WindowVis {
     return ((unsigned)(i - j) < (unsigned)window) && (i < sq) && (j < skv);
   }
 };
+
+#define MA_STEP() __builtin_amdgcn_sched_barrier(0)
+
+// Runs `step<MASKED>()` over a tile sequence, switching between the masked and the
+// unmasked variant only between runs of tiles, so each inner loop body is branch-free
+// (one basic block per variant; the accumulators never cross a branch join inside it).
+template <class Step, class IsFull>
+__device__ __forceinline__ void run_tiles(bool have, Step&& step, IsFull&& is_full) {
+  while (have) {
+    if (is_full()) {
+      do {
+        have = step(std::integral_constant<bool, false>{});
+      } while (have && is_full());
+    } else {
+      do {
+        have = step(std::integral_constant<bool, true>{});
+      } while (have && !is_full());
+    }
+  }
+}
 
 }  // namespace ma
