@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--workload", default="large_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-copy-probe", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (a kernel of known traffic, used to scale "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -172,6 +175,14 @@ def main():
         st = fn(*call_args)
         if st != 0:
             raise RuntimeError(f"backward failed with status {st}")
+
+    if args.with_copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

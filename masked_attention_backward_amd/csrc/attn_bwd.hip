@@ -139,7 +139,8 @@ struct BlockSource {
 //   steps 16-23: dV/dK of block 0, interleaved with the softmax of block 1 (4 chunks)
 //   steps 24-31: dV/dK of block 1
 // Operand fragments are loaded ahead of their MFMA, so LDS latency hides under the matrix
-// core while only a few fragments are live at once.
+// core while only a few fragments are live at once.  Global->LDS loads run two tiles ahead
+// (four LDS stages).
 template <class T, int NW>
 struct DkdvCtx {
   u32x4 kf[8], vf[8];
@@ -278,37 +279,45 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   const float sl2 = a.scale_log2;
   const int kj = c0 + 32 * w + c;
   FragOff fo(lane);
-  int stage = 0;
-  int hn = 0, tn = 0;
-  uint64_t bn = 0;
+  constexpr int KW = 2 * tile_loads_min<NW>();   // Q + dO instructions per tile and wave (at least)
+  auto fetch = [&](TileRef& r) -> bool { return next(r.head, r.tile, r.bits); };
+  // Tiles i and i + 1 are in flight when tile i is computed; tile i + 2 is issued then.
+  TileRef cur{}, nxt{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur.head, cur.tile, gray_stage(0));
+  bool vnxt = vcur && fetch(nxt);
+  if (vnxt) issue(nxt.head, nxt.tile, gray_stage(1));
+  int it = 0;
   // Window tiles that need no mask: every (q, kv) of the pair lies inside the window.
   // Rows past the sequence end need none either (lse2 = +inf there), nor do key columns
   // past the end (never stored).
   auto is_full = [&]() -> bool {
     if constexpr (MASK == MASK_WINDOW)
-      return (tn * 64 - (c0 + BC - 1) >= 0) && (tn * 64 + 63 - c0 < a.window);
+      return (cur.tile * 64 - (c0 + BC - 1) >= 0) && (cur.tile * 64 + 63 - c0 < a.window);
     else
-      return bn == ~0ull;
+      return cur.bits == ~0ull;
   };
   auto step = [&](auto masked) -> bool {
     constexpr bool MASKED = decltype(masked)::value;
-    const int t = tn;
-    const uint64_t bits = bn;
-    wait_async_loads();
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    const bool more = next(hn, tn, bn);
-    if (more) issue(hn, tn, stage ^ 1);
-    const int qdiff = t * 64 + 4 * h - kj;
-    const uint64_t hbits = h ? (bits >> 4) : bits;
-    dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + stage * 128 + 4 * h, sl2, qdiff, a.window, hbits);
-    fo.flip();
-    stage ^= 1;
-    return more;
+    TileRef n2{};
+    const bool v2 = vnxt && fetch(n2);
+    if (v2) issue(n2.head, n2.tile, gray_stage(it + 2));
+    const int qdiff = cur.tile * 64 + 4 * h - kj;
+    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
+    dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + gray_stage(it) * 128 + 4 * h, sl2, qdiff, a.window,
+                                      hbits);
+    fo.advance(it);
+    ++it;
+    cur = nxt;
+    vcur = vnxt;
+    nxt = n2;
+    vnxt = v2;
+    return vcur;
   };
-
-  bool have = next(hn, tn, bn);
-  if (have) issue(hn, tn, 0);
-  run_tiles(have, step, is_full);
+  run_tiles(vcur, step, is_full);
 
   // Epilogue: rows c0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
@@ -328,8 +337,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float sld[2 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float sld[NSTAGES * 128];
   const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
@@ -473,37 +482,43 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 
   const float sl2 = a.scale_log2;
   FragOff fo(lane);
-  int stage = 0;
-  int hn = 0, tn = 0;
-  uint64_t bn = 0;
+  constexpr int KW = 2 * tile_loads_min<NW>();   // K + V instructions per tile and wave (at least)
+  auto fetch = [&](TileRef& r) -> bool { return next(r.head, r.tile, r.bits); };
+  TileRef cur{}, nxt{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur.tile, gray_stage(0));
+  bool vnxt = vcur && fetch(nxt);
+  if (vnxt) issue(nxt.tile, gray_stage(1));
+  int it = 0;
   // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
   // workgroup (query rows past the end are never stored; key rows past the end always
   // fail the window test since Sq == Skv on the window path).
   auto is_full = [&]() -> bool {
     if constexpr (MASK == MASK_WINDOW)
-      return (r0 - (tn * 64 + 63) >= 0) && (r0 + BQ - 1 - tn * 64 < a.window);
+      return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
     else
-      return bn == ~0ull;
+      return cur.bits == ~0ull;
   };
   auto step = [&](auto masked) -> bool {
     constexpr bool MASKED = decltype(masked)::value;
-    const int t = tn;
-    const uint64_t bits = bn;
-    wait_async_loads();
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    const bool more = next(hn, tn, bn);
-    if (more) issue(tn, stage ^ 1);
-    const int kdiff = qi - t * 64 - 4 * h;
-    const uint64_t hbits = h ? (bits >> 4) : bits;
+    TileRef n2{};
+    const bool v2 = vnxt && fetch(n2);
+    if (v2) issue(n2.tile, gray_stage(it + 2));
+    const int kdiff = qi - cur.tile * 64 - 4 * h;
+    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
     dq_compute<T, MASK, MASKED>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits);
-    fo.flip();
-    stage ^= 1;
-    return more;
+    fo.advance(it);
+    ++it;
+    cur = nxt;
+    vcur = vnxt;
+    nxt = n2;
+    vnxt = v2;
+    return vcur;
   };
-
-  bool have = next(hn, tn, bn);
-  if (have) issue(tn, 0);
-  run_tiles(have, step, is_full);
+  run_tiles(vcur, step, is_full);
 
   // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
@@ -519,7 +534,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
   const int nbh = a.B * a.Hq;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;

@@ -80,23 +80,30 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 
   const float sl2 = a.scale_log2;
   FragOff fo(lane);
-  int stage = 0;
-  int tn = 0;
-  uint64_t bn = 0;
+  constexpr int KW = 2 * tile_loads_min<NW>();
+  auto fetch = [&](TileRef& r) -> bool { return next(r.tile, r.bits); };
+  TileRef cur{}, nxt{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur.tile, gray_stage(0));
+  bool vnxt = vcur && fetch(nxt);
+  if (vnxt) issue(nxt.tile, gray_stage(1));
+  int itx = 0;
   auto is_full = [&]() -> bool {
     if constexpr (MASK == MASK_WINDOW)
-      return (r0 - (tn * 64 + 63) >= 0) && (r0 + BQ - 1 - tn * 64 < a.window);
+      return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
     else
-      return bn == ~0ull;
+      return cur.bits == ~0ull;
   };
   auto step = [&](auto masked) -> bool {
     constexpr bool MASKED = decltype(masked)::value;
-    const int t = tn;
-    const uint64_t bits = bn;
-    wait_async_loads();
+    const int t = cur.tile;
+    const uint64_t bits = cur.bits;
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    const bool more = next(tn, bn);
-    if (more) issue(tn, stage ^ 1);
+    TileRef n2{};
+    const bool v2 = vnxt && fetch(n2);
+    if (v2) issue(n2.tile, gray_stage(itx + 2));
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -151,14 +158,15 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(frag_col(stages, fo, 1, t4, nb), pb, acc[nb]);
     }
-    fo.flip();
-    stage ^= 1;
-    return more;
+    fo.advance(itx);
+    ++itx;
+    cur = nxt;
+    vcur = vnxt;
+    nxt = n2;
+    vnxt = v2;
+    return vcur;
   };
-
-  bool have = next(tn, bn);
-  if (have) issue(tn, 0);
-  run_tiles(have, step, is_full);
+  run_tiles(vcur, step, is_full);
 
   // Epilogue: lane (c, h) holds O^T[d = nb*32 + 8(r/4) + 4h + r%4][q = qi].
   if (qi < q_end) {
@@ -180,7 +188,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[4 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
   const int nbh = a.B * a.Hq;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;

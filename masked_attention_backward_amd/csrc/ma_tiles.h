@@ -26,11 +26,19 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// Staged operand tiles live in one LDS array of two stages x two tiles (A, B): tile k of
-// stage s starts at byte (2 s + k) * 16384, so switching stage is one XOR of bit 15 in the
-// lane's offsets.
+// Staged operand tiles live in one LDS array of four stages x two tiles (A, B): tile k of
+// stage s starts at byte (2 s + k) * 16384.  Tiles are assigned to stages in Gray-code order
+// (tile i uses stage g(i) = j ^ (j >> 1) with j = i mod 4: 0, 1, 3, 2, 0, ...), so moving to the next
+// tile's stage is one XOR of the lane's offsets, alternately by 32 KiB and 64 KiB, and the
+// loads of tile i + 2 go to a stage nobody reads any more.
 constexpr int TILE_BYTES = TILE_ELEMS * 2;     // 16384
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // 32768
+constexpr int NSTAGES = 4;
+
+__device__ __forceinline__ int gray_stage(int i) {
+  const int j = i & 3;
+  return j ^ (j >> 1);
+}
 
 // Lane-dependent byte offsets of the MFMA operand fragments inside the staged tiles, with
 // the current stage folded in.  Every fragment read is one of these offsets plus a
@@ -58,12 +66,13 @@ struct FragOff {
       col[2 * nb + 1] = 2 * tile_off(8 + 4 * h + rin, 32 * nb + cs);
     }
   }
-  // Switch to the other stage.
-  __device__ __forceinline__ void flip() {
+  // Move from the stage of tile `it` to the stage of tile it + 1.
+  __device__ __forceinline__ void advance(int it) {
+    const int x = (it & 1) ? 2 * STAGE_BYTES : STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      row[i] ^= STAGE_BYTES;
-      col[i] ^= STAGE_BYTES;
+      row[i] ^= x;
+      col[i] ^= x;
     }
   }
 };
@@ -120,8 +129,24 @@ __device__ __forceinline__ void row_load_async(float* dst, const float* src, int
   __builtin_amdgcn_global_load_lds(src + lane, (lds_void_ptr)dst, 4, 0, 0);
 }
 
-// Wait for this wave's outstanding global->LDS loads.
-__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are outstanding (they
+// complete in issue order, so everything issued before the last N is done).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Number of global->LDS instructions a wave issues for one 64 x 128 tile (the smallest over
+// the waves of an NW-wave workgroup).
+template <int NW>
+constexpr int tile_loads_min() {
+  return 16 / NW;
+}
+
+struct TileRef {
+  int head, tile;
+  uint64_t bits;
+};
 
 // Visibility of the elements of one (query-tile, key-tile) pair.
 //   window:  query i sees key j iff 0 <= i - j < window, both inside their sequences
