@@ -133,99 +133,157 @@ struct BlockSource {
 //       lane column = key row, registers = query rows)
 //   dV[kv][d] += P^T dO        A = P^T (repacked accumulator), B = dO columns (tr read)
 //   dK[kv][d] += dS^T Q        A = dS^T,                       B = Q columns (tr read)
-// The instruction stream of one tile is laid out by hand (sched_barrier between steps):
-//   steps 0-7:   S/dP of block 0
-//   steps 8-15:  S/dP of block 1, interleaved with the softmax of block 0 (4 chunks)
-//   steps 16-23: dV/dK of block 0, interleaved with the softmax of block 1 (4 chunks)
-//   steps 24-31: dV/dK of block 1
-// Operand fragments are loaded ahead of their MFMA, so LDS latency hides under the matrix
-// core while only a few fragments are live at once.  Global->LDS loads run two tiles ahead
-// (four LDS stages).
+// The instruction stream of one tile is a program of 64 slots, one MFMA each, separated
+// by scheduling barriers (one wave per SIMD issues in order, so the work placed between
+// two MFMAs has to fit in the 32 cycles the matrix core spends on one of them):
+//   slots  0-15  S/dP of block 0            (slot 2k: S k-step k, slot 2k+1: dP k-step k)
+//   slots 16-31  S/dP of block 1
+//   slots 32-47  dV/dK of block 0           (slot 32+2j: dV, 32+2j+1: dK; j = 4 t4 + nb)
+//   slots 48-63  dV/dK of block 1
+// Every operand read from LDS is issued four slots before its MFMA.  The softmax of a
+// block is done one accumulator row (register r) per slot, spread over the slots between
+// the end of the block's S/dP and the first dV/dK slot that consumes the row's k-step
+// (the row timetable below); lse2/Delta of each group of four rows are read from LDS
+// three slots before the group's first row.  The global->LDS loads of the tile two ahead
+// are spread over the slots as well.
 template <class T, int NW>
 struct DkdvCtx {
   u32x4 kf[8], vf[8];
   f32x16 dk[4], dv[4];
 };
 
-// One quarter of a block's softmax: rows 8 g4 + 4 h + e (e = 0..3) of block mb; writes
-// k-slots 4 (g4 % 2) .. +3 of the P^T / dS^T operands of k-step g4 / 2 of the block.
-// `ld` points at this stage's lse2 row (64 floats) followed by its Delta row (64 floats).
-template <class T, int MASK, bool MASKED>
-__device__ __forceinline__ void dkdv_softmax_chunk(const f32x16& s, const f32x16& dp, u32x4* pa, u32x4* da,
-                                                   const float* ld, int mb, int g4, float sl2, int qdiff, int window,
-                                                   uint64_t hbits) {
-  const int qo = mb * 32 + 8 * g4;
-  const float4 L = *reinterpret_cast<const float4*>(ld + qo);
-  const float4 Dd = *reinterpret_cast<const float4*>(ld + 64 + qo);
-  const float Lv[4] = {L.x, L.y, L.z, L.w};
-  const float Dv[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
-  float p[4], ds[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * g4 + e;
-    float v = fast_exp2(fmaf(s[r], sl2, -Lv[e]));
-    if constexpr (MASKED) {
-      bool vis;
-      if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(qdiff + qo + e) < (unsigned)window;
-      else vis = (hbits >> (qo + e)) & 1ull;
-      v = vis ? v : 0.f;
-    }
-    p[e] = v;
-    ds[e] = v * (dp[r] - Dv[e]);
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
-  pa[g4 >> 1][2 * (g4 & 1)] = T::pack2(p[0], p[1]);
-  pa[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(p[2], p[3]);
-  da[g4 >> 1][2 * (g4 & 1)] = T::pack2(ds[0], ds[1]);
-  da[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(ds[2], ds[3]);
 }
 
-// One tile: tile A of the stage = Q, tile B = dO.
-template <class T, int MASK, int NW, bool MASKED>
-__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const uint16_t* stages,
-                                             const float* ld, float sl2, int qdiff, int window, uint64_t hbits) {
-  f32x16 s0, d0, s1, d1;
-  u32x4 qa[2], oa[2];
-  qa[0] = frag_row(stages, fo, 0, 0, 0);
-  oa[0] = frag_row(stages, fo, 1, 0, 0);
-  qa[1] = frag_row(stages, fo, 0, 1, 0);
-  oa[1] = frag_row(stages, fo, 1, 1, 0);
-  u32x4 pa0[2], da0[2], pa1[2], da1[2];
-  MA_STEP();
-#pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int mb = st >> 3, ks = st & 7;
-    f32x16& sc = mb ? s1 : s0;
-    f32x16& dc = mb ? d1 : d0;
-    sc = T::mma(qa[st & 1], x.kf[ks], ks ? sc : zero16());
-    dc = T::mma(oa[st & 1], x.vf[ks], ks ? dc : zero16());
-    if (st + 2 < 16) {
-      qa[st & 1] = frag_row(stages, fo, 0, (st + 2) & 7, (st + 2) >> 3);
-      oa[st & 1] = frag_row(stages, fo, 1, (st + 2) & 7, (st + 2) >> 3);
-    }
-    if (mb == 1 && (ks & 1) == 0)
-      dkdv_softmax_chunk<T, MASK, MASKED>(s0, d0, pa0, da0, ld, 0, ks >> 1, sl2, qdiff, window, hbits);
-    MA_STEP();
-  }
-  u32x4 bo[2], bq[2];
-  bo[0] = frag_col(stages, fo, 1, 0, 0);
-  bq[0] = frag_col(stages, fo, 0, 0, 0);
-  MA_STEP();
-#pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int t4 = st >> 2, nb = st & 3;
-    if (st + 1 < 16) {
-      bo[(st + 1) & 1] = frag_col(stages, fo, 1, (st + 1) >> 2, (st + 1) & 3);
-      bq[(st + 1) & 1] = frag_col(stages, fo, 0, (st + 1) >> 2, (st + 1) & 3);
-    }
-    const u32x4& pa = t4 < 2 ? pa0[t4] : pa1[t4 - 2];
-    const u32x4& da = t4 < 2 ? da0[t4] : da1[t4 - 2];
-    x.dv[nb] = T::mma(pa, bo[st & 1], x.dv[nb]);
-    x.dk[nb] = T::mma(da, bq[st & 1], x.dk[nb]);
-    if (st < 8 && (st & 1) == 0)
-      dkdv_softmax_chunk<T, MASK, MASKED>(s1, d1, pa1, da1, ld, 1, st >> 1, sl2, qdiff, window, hbits);
-    MA_STEP();
-  }
+// Slot of the softmax of accumulator row r of block mb (block 0: rows on two of every
+// three slots from 17; block 1: the two free slots left before 40, then one row per
+// slot).  A row pair (r, r+1) is packed into the operands right after row r+1.
+__host__ __device__ constexpr int dkdv_row_slot(int mb, int r) {
+  return mb == 0 ? 17 + (3 * r) / 2 : (r == 0 ? 34 : r == 1 ? 37 : 38 + r);
 }
+constexpr int DKDV_LA = 4;        // LDS operand reads run this many slots ahead
+constexpr int DKDV_LD_LEAD = 3;   // lse2/Delta reads run this many slots ahead of a group
+
+// Is slot `s` the one that issues load instruction i of NI (spread over the tile)?
+__host__ __device__ constexpr bool dkdv_dma_at(int i, int ni, int s) { return ((i * 32) / ni) * 2 + 1 == s; }
+
+// One tile: tile A of the stage = Q, tile B = dO.  `nx` issues the loads of the tile two
+// ahead.  `ld` points at this stage's lse2 row (64 floats) followed by its Delta row.
+template <class T, int MASK, int NW, bool MASKED, class Next>
+__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const uint16_t* stages,
+                                             const float* ld, float sl2, int qdiff, int window, uint64_t hbits,
+                                             const Next& nx) {
+  constexpr int NI = Next::COUNT;
+  constexpr int LA = DKDV_LA;
+  f32x16 sacc[2], dacc[2];       // S and dP of blocks 0 and 1
+  u32x4 fr[LA];                  // operand fragments in flight
+  u32x4 pa[2][2], da[2][2];      // P^T and dS^T operands: [block][k-step of 16 rows]
+  f32x4 Lg[2][2], Dg[2][2];      // lse2 / Delta of row groups: [block][group parity]
+  float pk[2], dk2[2];           // first row of a pair, per block
+
+  // Operand of slot s: row fragments for S/dP, column fragments for dV/dK.
+  auto frag = [&](auto sc) -> u32x4 {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s < 32) return frag_row(stages, fo, s & 1, (s % 16) / 2, s / 16);
+    else {
+      constexpr int k = s - 32;
+      return frag_col(stages, fo, (k & 1) ? 0 : 1, k / 8, (k % 8) / 2);
+    }
+  };
+  static_for<0, LA>([&](auto sc) { fr[decltype(sc)::value] = frag(sc); });
+  MA_STEP();
+  static_for<0, 64>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    // The MFMA of this slot.
+    if constexpr (s < 32) {
+      constexpr int mb = s / 16, ks = (s % 16) / 2;
+      if constexpr ((s & 1) == 0)
+        sacc[mb] = T::mma(fr[s % LA], x.kf[ks], ks ? sacc[mb] : zero16());
+      else
+        dacc[mb] = T::mma(fr[s % LA], x.vf[ks], ks ? dacc[mb] : zero16());
+    } else {
+      constexpr int k = s - 32, j = k / 2, t4 = j / 4, nb = j % 4;
+      if constexpr ((k & 1) == 0)
+        x.dv[nb] = T::mma(pa[t4 / 2][t4 % 2], fr[s % LA], x.dv[nb]);
+      else
+        x.dk[nb] = T::mma(da[t4 / 2][t4 % 2], fr[s % LA], x.dk[nb]);
+    }
+    // Operand read for slot s + LA.
+    if constexpr (s + LA < 64) fr[(s + LA) % LA] = frag(std::integral_constant<int, s + LA>{});
+    // lse2/Delta of a row group whose first row comes DKDV_LD_LEAD slots from now.
+    static_for<0, 2>([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
+      static_for<0, 4>([&](auto gc) {
+        constexpr int g4 = decltype(gc)::value;
+        if constexpr (dkdv_row_slot(mb, 4 * g4) - DKDV_LD_LEAD == s) {
+          // volatile keeps the reads in this slot (they would otherwise be moved next to
+          // their first use and waited for there)
+          typedef const volatile __attribute__((address_space(3))) f32x4* lds_f32x4;
+          Lg[mb][g4 & 1] = *(lds_f32x4)(ld + mb * 32 + 8 * g4);
+          Dg[mb][g4 & 1] = *(lds_f32x4)(ld + 64 + mb * 32 + 8 * g4);
+        }
+      });
+    });
+    // Softmax rows of this slot.
+    static_for<0, 2>([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (dkdv_row_slot(mb, r) == s) {
+          constexpr int e = r % 4;
+          const float L = Lg[mb][(r / 4) & 1][e];
+          const float D = Dg[mb][(r / 4) & 1][e];
+          float v = fast_exp2(fmaf(sacc[mb][r], sl2, -L));
+          if constexpr (MASKED) {
+            constexpr int qo = mb * 32 + 8 * (r / 4) + e;
+            bool vis;
+            if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(qdiff + qo) < (unsigned)window;
+            else vis = (hbits >> qo) & 1ull;
+            v = vis ? v : 0.f;
+          }
+          const float d = v * (dacc[mb][r] - D);
+          if constexpr ((r & 1) == 0) {
+            pk[mb] = v;
+            dk2[mb] = d;
+          } else {
+            pa[mb][r / 8][(r % 8) / 2] = T::pack2(pk[mb], v);
+            da[mb][r / 8][(r % 8) / 2] = T::pack2(dk2[mb], d);
+          }
+        }
+      });
+    });
+    // Global->LDS loads of the tile two ahead.
+    static_for<0, NI>([&](auto ic) {
+      if constexpr (dkdv_dma_at(decltype(ic)::value, NI, s)) nx.issue(decltype(ic)::value);
+    });
+    MA_STEP();
+  });
+}
+
+// Loads of one dK/dV stage: instruction 0 = the lse2 row (wave 0) and the Delta row
+// (wave NW-1), then the Q and dO tiles.
+template <int NW>
+struct DkdvNext {
+  static constexpr int COUNT = 1 + 2 * StageLoads<NW>::J;
+  StageLoads<NW> tiles;
+  const float* lse2;
+  const float* delta;
+  float* rows;
+  int w, lane;
+  __device__ __forceinline__ void issue(int i) const {
+    if (i == 0) {
+      if (w == 0) row_load_async(rows, lse2, lane);
+      if (w == NW - 1) row_load_async(rows + 64, delta, lane);
+    } else {
+      tiles.issue(i - 1, w);
+    }
+  }
+};
 
 template <class T, int MASK, int NW>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kb,
@@ -266,14 +324,23 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
     else return bsrc.next(hd, t, bits);
   };
-  // Prefetch tile (hd, t) into stage `stg`: Q -> tile A, dO -> tile B, lse2/Delta rows.
-  auto issue = [&](int hd, int t, int stg) {
-    const size_t qhead = (size_t)b * a.Hq + hd;
-    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
-    tile_load_async<NW>(dst, (const uint16_t*)a.q + qhead * a.Sq * HD, t * 64, a.Sq, w, lane);
-    tile_load_async<NW>(dst + TILE_ELEMS, (const uint16_t*)a.dout + qhead * a.Sq * HD, t * 64, a.Sq, w, lane);
-    if (w == 0) row_load_async(sld + stg * 128, a.lse2 + qhead * sq_pad + t * 64, lane);
-    if (w == NW - 1) row_load_async(sld + stg * 128 + 64, a.delta + qhead * sq_pad + t * 64, lane);
+  // Loads of tile (hd, t) into stage `stg`: Q -> tile A, dO -> tile B, lse2/Delta rows.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  DkdvNext<NW> nx;
+  nx.w = wu;
+  nx.lane = lane;
+  auto prepare = [&](const TileRef& r, int stg) {
+    const size_t qhead = (size_t)b * a.Hq + r.head;
+    nx.tiles.prepare((const uint16_t*)a.q + qhead * a.Sq * HD, (const uint16_t*)a.dout + qhead * a.Sq * HD,
+                     stages + stg * (2 * TILE_ELEMS), r.tile * 64, a.Sq, wu, lane);
+    nx.lse2 = a.lse2 + qhead * sq_pad + r.tile * 64;
+    nx.delta = a.delta + qhead * sq_pad + r.tile * 64;
+    nx.rows = sld + stg * 128;
+  };
+  auto issue_all = [&](const TileRef& r, int stg) {
+    prepare(r, stg);
+#pragma unroll
+    for (int i = 0; i < DkdvNext<NW>::COUNT; ++i) nx.issue(i);
   };
 
   const float sl2 = a.scale_log2;
@@ -284,9 +351,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   // Tiles i and i + 1 are in flight when tile i is computed; tile i + 2 is issued then.
   TileRef cur{}, nxt{};
   bool vcur = fetch(cur);
-  if (vcur) issue(cur.head, cur.tile, gray_stage(0));
+  if (vcur) issue_all(cur, gray_stage(0));
   bool vnxt = vcur && fetch(nxt);
-  if (vnxt) issue(nxt.head, nxt.tile, gray_stage(1));
+  if (vnxt) issue_all(nxt, gray_stage(1));
   int it = 0;
   // Window tiles that need no mask: every (q, kv) of the pair lies inside the window.
   // Rows past the sequence end need none either (lse2 = +inf there), nor do key columns
@@ -304,11 +371,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     __syncthreads();
     TileRef n2{};
     const bool v2 = vnxt && fetch(n2);
-    if (v2) issue(n2.head, n2.tile, gray_stage(it + 2));
+    // Without a tile two ahead the loads repeat the current one into the free stage, which
+    // keeps the step free of branches; they are drained before the workgroup moves on.
+    prepare(v2 ? n2 : cur, gray_stage(it + 2));
     const int qdiff = cur.tile * 64 + 4 * h - kj;
     const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
     dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + gray_stage(it) * 128 + 4 * h, sl2, qdiff, a.window,
-                                      hbits);
+                                      hbits, nx);
     fo.advance(it);
     ++it;
     cur = nxt;
@@ -318,6 +387,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     return vcur;
   };
   run_tiles(vcur, step, is_full);
+  wait_vmcnt<0>();
 
   // Epilogue: rows c0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;

@@ -101,6 +101,27 @@ __device__ __forceinline__ u32x4 frag_col(const uint16_t* stages, const FragOff&
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
+}
+
+// Global -> LDS copies (LDS DMA): the wave-instruction reads 16 bytes (4 bytes for dma4)
+// per lane from sbase + voff and writes them, lane after lane, to LDS starting at byte
+// address `lds` (taken from M0).  They are issued from inline assembly on purpose: the
+// compiler would treat each one as a possible write to any later-read LDS location and
+// wait for it to complete before the next LDS read, which serialises the whole
+// prefetch.  The kernels order these copies against their LDS reads themselves: an
+// explicit vmcnt wait by every wave, then a workgroup barrier, before a stage is read.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+
 // Cooperative load of one 64 x 128 tile (rows clamped into [0, nrows), row stride HD)
 // straight from global memory into a swizzled LDS tile (global_load_lds_dwordx4: each
 // wave-instruction fills 1 KiB = 4 rows of LDS, lane i writing bytes [16 i, 16 i + 16) of
@@ -117,8 +138,8 @@ __device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* 
       const int row = 4 * u + (lane >> 4);
       const int p = lane & 15;
       const int g = min(row0 + row, nrows - 1);
-      const uint16_t* src = base + (size_t)g * HD + ((p ^ swz(row)) << 3);
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(tile + u * 512), 16, 0, 0);
+      const uint32_t off = 2u * (uint32_t)(g * HD + ((p ^ swz(row)) << 3));
+      dma16(base, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + u * 512)));
     }
   }
 }
@@ -126,8 +147,43 @@ __device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* 
 // 64 consecutive fp32 values straight into LDS by one wave (the per-row buffers are
 // padded to a multiple of 64 rows).
 __device__ __forceinline__ void row_load_async(float* dst, const float* src, int lane) {
-  __builtin_amdgcn_global_load_lds(src + lane, (lds_void_ptr)dst, 4, 0, 0);
+  dma4(src, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
 }
+
+// The global->LDS loads of one stage (tile A and tile B of 64 rows each, same rows of two
+// tensors), prepared once and then issued one wave-instruction at a time, so that a wave
+// can spread them over the matrix-core work of the tile it is computing instead of
+// queueing all of them on the memory pipeline at once.  Instruction i < J fills rows
+// [4u, 4u + 4) of tile A, u = w + i NW; instruction J + i does the same for tile B.
+template <int NW>
+struct StageLoads {
+  static constexpr int J = (16 + NW - 1) / NW;   // instructions per tile for wave 0
+  const uint16_t* srca;                          // head base of tensor A (wave-uniform)
+  const uint16_t* srcb;                          // head base of tensor B
+  uint16_t* dst;                                 // LDS stage (tile A; tile B follows)
+  uint32_t off[J];                               // this lane's byte offset per instruction
+
+  __device__ __forceinline__ void prepare(const uint16_t* a, const uint16_t* b, uint16_t* stage, int row0, int nrows,
+                                          int w, int lane) {
+    srca = a;
+    srcb = b;
+    dst = stage;
+    const int p = lane & 15;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int row = 4 * (w + j * NW) + (lane >> 4);
+      off[j] = 2u * (uint32_t)(min(row0 + row, nrows - 1) * HD + ((p ^ swz(row)) << 3));
+    }
+  }
+  // Number of instructions wave w issues (issue(i) for i >= count(w) does nothing).
+  __device__ __forceinline__ static constexpr bool exists(int j, int w) { return (16 % NW) == 0 || w + j * NW < 16; }
+  __device__ __forceinline__ void issue(int i, int w) const {
+    const int j = i < J ? i : i - J;
+    if (!exists(j, w)) return;
+    uint16_t* d = dst + (i < J ? 0 : TILE_ELEMS) + (w + j * NW) * 512;
+    dma16(i < J ? srca : srcb, off[j], __builtin_amdgcn_readfirstlane(lds_addr(d)));
+  }
+};
 
 // Wait until at most N of this wave's vector-memory operations are outstanding (they
 // complete in issue order, so everything issued before the last N is done).
