@@ -18,7 +18,17 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmaskattn.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["capi.hip", "attn_bwd.hip", "attn_fwd.hip", "mask_tables.hip"]
+# (source, object name, preprocessor definitions).  attn_bwd_variant.hip is compiled once
+# per dK/dV + dQ kernel variant the dispatch uses (dtype x mask kind x waves), so the large
+# unrolled kernels build in parallel.
+SOURCES = [("capi.hip", "capi", []), ("attn_bwd.hip", "attn_bwd", []), ("attn_fwd.hip", "attn_fwd", []),
+           ("mask_tables.hip", "mask_tables", [])]
+for _dt, _dtn in ((0, "f16"), (1, "bf16")):
+    SOURCES.append(("attn_bwd_variant.hip", f"bwd_{_dtn}_window_nw4",
+                    [f"-DMA_VARIANT_DTYPE={_dt}", "-DMA_VARIANT_MASK=0", "-DMA_VARIANT_NW=4"]))
+    for _nw in (1, 2, 3, 4):
+        SOURCES.append(("attn_bwd_variant.hip", f"bwd_{_dtn}_block_nw{_nw}",
+                        [f"-DMA_VARIANT_DTYPE={_dt}", "-DMA_VARIANT_MASK=1", f"-DMA_VARIANT_NW={_nw}"]))
 
 ARCH = "gfx950"
 FLAGS = [
@@ -41,9 +51,10 @@ def _hipcc():
     return exe
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry, verbose):
+    src, name, defs = entry
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [_hipcc(), *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,7 +65,7 @@ def _compile(src, verbose):
 
 def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    jobs = jobs or min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"

@@ -1,0 +1,571 @@
+// Attention backward kernels for gfx950: preprocess (Delta, dsink partials), a fixed-order
+// dsink reduce, a key/value-tile-stationary dK/dV kernel and a query-tile-stationary dQ
+// kernel.  Both main kernels recompute S = scale*Q K^T and P = exp(S - lse) tile by tile
+// (the FlashAttention-style recompute of the five-GEMM backward: S, P, dV += P^T dO,
+// dP = dO V^T, dS = P (dP - Delta), dK += dS^T Q, dQ += dS K), as described on the page
+// "[Example] Add GQA Sink Backward BHSD ..." (commit of the 9->6 kernel revision: QK^T,
+// softmax, dV+dP, dS, dK+dQ; commit of the 4->2 revision: Delta = sum(O*dO), five GEMMs,
+// dSink) and on the page "knowledge(triton) ... #174" (BlockSparseAttentionGrad skeleton:
+// delta, then dq over the q-major table, then dk/dv over the kv-major table).
+//
+// Design on CDNA4, differing from the pages' Ascend kernels:
+//   * dK/dV accumulate in registers of the workgroup that owns the key tile, and dQ in
+//     the workgroup that owns the query tile, so there are no atomics and no fp32
+//     partial buffers: results are bit-identical run to run (the pages' single-kernel
+//     revision accumulated dK/dV with fp32 atomics and a host-side cast).
+//   * P and dS never leave registers: the accumulator tile of S^T (or S) is re-packed in
+//     place as the A/B operand of the next MFMA, with the contraction index permuted to
+//     match (see ma_device.h), and the other operand is read down the columns of the
+//     staged tile with ds_read_b64_tr_b16.
+//   * Q/dO (or K/V) tiles are double-buffered in LDS; the next tile's global loads are
+//     issued before the current tile's MFMAs.
+#pragma once
+
+#include "ma_launch.h"
+#include "ma_tiles.h"
+
+namespace ma {
+
+// ------------------------------------------------------------------ tile sources
+// Sequence of (query head, 64-row tile, row bitmask) a stationary workgroup visits.
+struct WindowSource {
+  int head0, nheads, tlo, nt, it;
+  __device__ bool next(int& head, int& tile, uint64_t& bits) {
+    if (it >= nheads * nt) return false;
+    head = head0 + it / nt;
+    tile = tlo + it % nt;
+    bits = 0;
+    ++it;
+    return true;
+  }
+};
+
+struct BlockSource {
+  TileWalker walk;
+  int head;
+  __device__ bool next(int& hd, int& tile, uint64_t& bits) {
+    hd = head;
+    return walk.next(tile, bits);
+  }
+};
+
+// ----------------------------------------------------------------------- dK / dV
+// Workgroup = NW waves owning 32*NW consecutive key rows (wave w: rows c0+32w .. +32).
+// Per visited (query head, query tile of 64 rows), in two 32-row query blocks mb:
+//   S[q][kv]  = Q K^T          A = Q rows (LDS),   B = K rows (registers)
+//   dP[q][kv] = dO V^T         A = dO rows (LDS),  B = V rows (registers)
+//   P = exp2(S*scale*log2e - lse*log2e), dS = P (dP - Delta)   (accumulator layout:
+//       lane column = key row, registers = query rows)
+//   dV[kv][d] += P^T dO        A = P^T (repacked accumulator), B = dO columns (tr read)
+//   dK[kv][d] += dS^T Q        A = dS^T,                       B = Q columns (tr read)
+// The instruction stream of one tile is a program of 64 slots, one MFMA each, separated
+// by scheduling barriers (one wave per SIMD issues in order, so the work placed between
+// two MFMAs has to fit in the 32 cycles the matrix core spends on one of them):
+//   slots  0-15  S/dP of block 0            (slot 2k: S k-step k, slot 2k+1: dP k-step k)
+//   slots 16-31  S/dP of block 1
+//   slots 32-47  dV/dK of block 0           (slot 32+2j: dV, 32+2j+1: dK; j = 4 t4 + nb)
+//   slots 48-63  dV/dK of block 1
+// Every operand read from LDS is issued four slots before its MFMA.  The softmax of a
+// block is done one accumulator row (register r) per slot, spread over the slots between
+// the end of the block's S/dP and the first dV/dK slot that consumes the row's k-step
+// (the row timetable below); lse2/Delta of each group of four rows are read from LDS
+// three slots before the group's first row.  The global->LDS loads of the tile two ahead
+// are spread over the slots as well.
+template <class T, int NW>
+struct DkdvCtx {
+  u32x4 kf[8], vf[8];
+  f32x16 dk[4], dv[4];
+};
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Slot of the softmax of accumulator row r of block mb (block 0: rows on two of every
+// three slots from 17; block 1: the two free slots left before 40, then one row per
+// slot).  A row pair (r, r+1) is packed into the operands right after row r+1.
+__host__ __device__ constexpr int dkdv_row_slot(int mb, int r) {
+  return mb == 0 ? 17 + (3 * r) / 2 : (r == 0 ? 34 : r == 1 ? 37 : 38 + r);
+}
+constexpr int DKDV_LA = 4;        // LDS operand reads run this many slots ahead
+constexpr int DKDV_LD_LEAD = 3;   // lse2/Delta reads run this many slots ahead of a group
+
+// Is slot `s` the one that issues load instruction i of NI (spread over the tile)?
+__host__ __device__ constexpr bool dkdv_dma_at(int i, int ni, int s) { return ((i * 32) / ni) * 2 + 1 == s; }
+
+// One tile: tile A of the stage = Q, tile B = dO.  `nx` issues the loads of the tile two
+// ahead.  `ld` points at this stage's lse2 row (64 floats) followed by its Delta row.
+template <class T, int MASK, int NW, bool MASKED, class Next>
+__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const uint16_t* stages,
+                                             const float* ld, float sl2, int qdiff, int window, uint64_t hbits,
+                                             const Next& nx) {
+  constexpr int NI = Next::COUNT;
+  constexpr int LA = DKDV_LA;
+  f32x16 sacc[2], dacc[2];       // S and dP of blocks 0 and 1
+  u32x4 fr[LA];                  // operand fragments in flight
+  u32x4 pa[2][2], da[2][2];      // P^T and dS^T operands: [block][k-step of 16 rows]
+  f32x4 Lg[2][2], Dg[2][2];      // lse2 / Delta of row groups: [block][group parity]
+  float pk[2], dk2[2];           // first row of a pair, per block
+
+  // Operand of slot s: row fragments for S/dP, column fragments for dV/dK.
+  auto frag = [&](auto sc) -> u32x4 {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s < 32) return frag_row(stages, fo, s & 1, (s % 16) / 2, s / 16);
+    else {
+      constexpr int k = s - 32;
+      return frag_col(stages, fo, (k & 1) ? 0 : 1, k / 8, (k % 8) / 2);
+    }
+  };
+  static_for<0, LA>([&](auto sc) { fr[decltype(sc)::value] = frag(sc); });
+  MA_STEP();
+  static_for<0, 64>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    // The MFMA of this slot.
+    if constexpr (s < 32) {
+      constexpr int mb = s / 16, ks = (s % 16) / 2;
+      if constexpr ((s & 1) == 0)
+        sacc[mb] = T::mma(fr[s % LA], x.kf[ks], ks ? sacc[mb] : zero16());
+      else
+        dacc[mb] = T::mma(fr[s % LA], x.vf[ks], ks ? dacc[mb] : zero16());
+    } else {
+      constexpr int k = s - 32, j = k / 2, t4 = j / 4, nb = j % 4;
+      if constexpr ((k & 1) == 0)
+        x.dv[nb] = T::mma(pa[t4 / 2][t4 % 2], fr[s % LA], x.dv[nb]);
+      else
+        x.dk[nb] = T::mma(da[t4 / 2][t4 % 2], fr[s % LA], x.dk[nb]);
+    }
+    // Operand read for slot s + LA.
+    if constexpr (s + LA < 64) fr[(s + LA) % LA] = frag(std::integral_constant<int, s + LA>{});
+    // lse2/Delta of a row group whose first row comes DKDV_LD_LEAD slots from now.
+    static_for<0, 2>([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
+      static_for<0, 4>([&](auto gc) {
+        constexpr int g4 = decltype(gc)::value;
+        if constexpr (dkdv_row_slot(mb, 4 * g4) - DKDV_LD_LEAD == s) {
+          // volatile keeps the reads in this slot (they would otherwise be moved next to
+          // their first use and waited for there)
+          typedef const volatile __attribute__((address_space(3))) f32x4* lds_f32x4;
+          Lg[mb][g4 & 1] = *(lds_f32x4)(ld + mb * 32 + 8 * g4);
+          Dg[mb][g4 & 1] = *(lds_f32x4)(ld + 64 + mb * 32 + 8 * g4);
+        }
+      });
+    });
+    // Softmax rows of this slot.
+    static_for<0, 2>([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (dkdv_row_slot(mb, r) == s) {
+          constexpr int e = r % 4;
+          const float L = Lg[mb][(r / 4) & 1][e];
+          const float D = Dg[mb][(r / 4) & 1][e];
+          float v = fast_exp2(fmaf(sacc[mb][r], sl2, -L));
+          if constexpr (MASKED) {
+            constexpr int qo = mb * 32 + 8 * (r / 4) + e;
+            bool vis;
+            if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(qdiff + qo) < (unsigned)window;
+            else vis = (hbits >> qo) & 1ull;
+            v = vis ? v : 0.f;
+          }
+          const float d = v * (dacc[mb][r] - D);
+          if constexpr ((r & 1) == 0) {
+            pk[mb] = v;
+            dk2[mb] = d;
+          } else {
+            pa[mb][r / 8][(r % 8) / 2] = T::pack2(pk[mb], v);
+            da[mb][r / 8][(r % 8) / 2] = T::pack2(dk2[mb], d);
+          }
+        }
+      });
+    });
+    // Global->LDS loads of the tile two ahead.
+    static_for<0, NI>([&](auto ic) {
+      if constexpr (dkdv_dma_at(decltype(ic)::value, NI, s)) nx.issue(decltype(ic)::value);
+    });
+    MA_STEP();
+  });
+}
+
+// Loads of one dK/dV stage: instruction 0 = the lse2 row (wave 0) and the Delta row
+// (wave NW-1), then the Q and dO tiles.
+template <int NW>
+struct DkdvNext {
+  static constexpr int COUNT = 1 + 2 * StageLoads<NW>::J;
+  StageLoads<NW> tiles;
+  const float* lse2;
+  const float* delta;
+  float* rows;
+  int w, lane;
+  __device__ __forceinline__ void issue(int i) const {
+    if (i == 0) {
+      if (w == 0) row_load_async(rows, lse2, lane);
+      if (w == NW - 1) row_load_async(rows + 64, delta, lane);
+    } else {
+      tiles.issue(i - 1, w);
+    }
+  }
+};
+
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kb,
+                                          uint16_t* stages, float* sld) {
+  constexpr int BC = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
+
+  DkdvCtx<T, NW> x;
+  // This lane's key row (clamped into the sequence; rows past the end are never stored).
+  const int kr = min(c0 + 32 * w + c, a.Skv - 1);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    x.kf[ks] = ld16(Kp + (size_t)kr * HD + ks * 16 + 8 * h);
+    x.vf[ks] = ld16(Vp + (size_t)kr * HD + ks * 16 + 8 * h);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    x.dk[nb] = zero16();
+    x.dv[nb] = zero16();
+  }
+
+  WindowSource wsrc{};
+  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  if constexpr (MASK == MASK_WINDOW) {
+    const int qend = min(a.Sq, c0 + BC + a.window - 1);
+    const int tlo = c0 >> 6;
+    const int thi = (qend + 63) >> 6;
+    wsrc = WindowSource{kvh * a.group, a.group, tlo, max(0, thi - tlo), 0};
+  } else {
+    const size_t row = kvhead * a.nkb + kb;
+    bsrc = BlockSource{TileWalker(a.sel_k + row * a.nqb, a.cnt_k[row], a.bx, a.Sq), kvh};
+  }
+  auto next = [&](int& hd, int& t, uint64_t& bits) -> bool {
+    if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
+    else return bsrc.next(hd, t, bits);
+  };
+  // Loads of tile (hd, t) into stage `stg`: Q -> tile A, dO -> tile B, lse2/Delta rows.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  DkdvNext<NW> nx;
+  nx.w = wu;
+  nx.lane = lane;
+  auto prepare = [&](const TileRef& r, int stg) {
+    const size_t qhead = (size_t)b * a.Hq + r.head;
+    nx.tiles.prepare((const uint16_t*)a.q + qhead * a.Sq * HD, (const uint16_t*)a.dout + qhead * a.Sq * HD,
+                     stages + stg * (2 * TILE_ELEMS), r.tile * 64, a.Sq, wu, lane);
+    nx.lse2 = a.lse2 + qhead * sq_pad + r.tile * 64;
+    nx.delta = a.delta + qhead * sq_pad + r.tile * 64;
+    nx.rows = sld + stg * 128;
+  };
+  auto issue_all = [&](const TileRef& r, int stg) {
+    prepare(r, stg);
+#pragma unroll
+    for (int i = 0; i < DkdvNext<NW>::COUNT; ++i) nx.issue(i);
+  };
+
+  const float sl2 = a.scale_log2;
+  const int kj = c0 + 32 * w + c;
+  FragOff fo(lane);
+  constexpr int KW = 2 * tile_loads_min<NW>();   // Q + dO instructions per tile and wave (at least)
+  auto fetch = [&](TileRef& r) -> bool { return next(r.head, r.tile, r.bits); };
+  // Tiles i and i + 1 are in flight when tile i is computed; tile i + 2 is issued then.
+  TileRef cur{}, nxt{};
+  bool vcur = fetch(cur);
+  if (vcur) issue_all(cur, gray_stage(0));
+  bool vnxt = vcur && fetch(nxt);
+  if (vnxt) issue_all(nxt, gray_stage(1));
+  int it = 0;
+  // Window tiles that need no mask: every (q, kv) of the pair lies inside the window.
+  // Rows past the sequence end need none either (lse2 = +inf there), nor do key columns
+  // past the end (never stored).
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (cur.tile * 64 - (c0 + BC - 1) >= 0) && (cur.tile * 64 + 63 - c0 < a.window);
+    else
+      return cur.bits == ~0ull;
+  };
+  auto step = [&](auto masked) -> bool {
+    constexpr bool MASKED = decltype(masked)::value;
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    TileRef n2{};
+    const bool v2 = vnxt && fetch(n2);
+    // Without a tile two ahead the loads repeat the current one into the free stage, which
+    // keeps the step free of branches; they are drained before the workgroup moves on.
+    prepare(v2 ? n2 : cur, gray_stage(it + 2));
+    const int qdiff = cur.tile * 64 + 4 * h - kj;
+    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
+    dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + gray_stage(it) * 128 + 4 * h, sl2, qdiff, a.window,
+                                      hbits, nx);
+    fo.advance(it);
+    ++it;
+    cur = nxt;
+    vcur = vnxt;
+    nxt = n2;
+    vnxt = v2;
+    return vcur;
+  };
+  run_tiles(vcur, step, is_full);
+  wait_vmcnt<0>();
+
+  // Epilogue: rows c0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
+  uint16_t* dVp = (uint16_t*)a.dv + kvhead * a.Skv * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = c0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < kv_end) {
+        dKp[(size_t)row * HD + nb * 32 + c] = T::one(x.dk[nb][r] * a.scale);
+        dVp[(size_t)row * HD + nb * 32 + c] = T::one(x.dv[nb][r]);
+      }
+    }
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64) void dkdv_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float sld[NSTAGES * 128];
+  const int nbh = a.B * a.Hkv;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BC = 32 * NW;
+    dkdv_tile<T, MASK, NW>(a, b, kvh, p * BC, a.Skv, 0, stages, sld);
+    const int p2 = a.n_tiles - 1 - p;
+    if (a.pair && p2 != p) {
+      __syncthreads();
+      dkdv_tile<T, MASK, NW>(a, b, kvh, p2 * BC, a.Skv, 0, stages, sld);
+    }
+  } else {
+    const int c0 = p * a.by;
+    dkdv_tile<T, MASK, NW>(a, b, kvh, c0, min(c0 + a.by, a.Skv), p, stages, sld);
+  }
+}
+
+// --------------------------------------------------------------------------- dQ
+// Workgroup = NW waves owning 32*NW consecutive query rows (wave w: rows r0+32w .. +32).
+// Per visited key tile of 64 rows, in two 32-row key blocks mb:
+//   S^T[kv][q]  = K Q^T       A = K rows (LDS),  B = Q rows (registers)
+//   dP^T[kv][q] = V dO^T      A = V rows (LDS),  B = dO rows (registers)
+//   (accumulator layout: lane column = query row, registers = key rows)
+//   dQ[q][d] += dS K          A = dS (repacked accumulator), B = K columns (tr read)
+// Hand-laid stream as in dK/dV: S/dP of block 0; S/dP of block 1 + softmax of block 0;
+// dQ of block 0 + softmax of block 1; dQ of block 1.
+template <class T, int MASK, bool MASKED>
+__device__ __forceinline__ void dq_softmax_chunk(const f32x16& s, const f32x16& dp, u32x4* da, int mb, int g4,
+                                                 float sl2, float l2, float dd, int kdiff, int window,
+                                                 uint64_t hbits) {
+  float ds[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g4 + e;
+    const int ko = mb * 32 + 8 * g4 + e;
+    float v = fast_exp2(fmaf(s[r], sl2, -l2));
+    if constexpr (MASKED) {
+      bool vis;
+      if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
+      else vis = (hbits >> ko) & 1ull;
+      v = vis ? v : 0.f;
+    }
+    ds[e] = v * (dp[r] - dd);
+  }
+  da[g4 >> 1][2 * (g4 & 1)] = T::pack2(ds[0], ds[1]);
+  da[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(ds[2], ds[3]);
+}
+
+// One key tile: tile A of the stage = K, tile B = V.
+template <class T, int MASK, bool MASKED>
+__device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
+                                           const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
+                                           int window, uint64_t hbits) {
+  f32x16 s0, d0, s1, d1;
+  u32x4 ka[2], va[2];
+  ka[0] = frag_row(stages, fo, 0, 0, 0);
+  va[0] = frag_row(stages, fo, 1, 0, 0);
+  ka[1] = frag_row(stages, fo, 0, 1, 0);
+  va[1] = frag_row(stages, fo, 1, 1, 0);
+  u32x4 da0[2], da1[2];
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int mb = st >> 3, ks = st & 7;
+    f32x16& sc = mb ? s1 : s0;
+    f32x16& dc = mb ? d1 : d0;
+    sc = T::mma(ka[st & 1], qf[ks], ks ? sc : zero16());
+    dc = T::mma(va[st & 1], of[ks], ks ? dc : zero16());
+    if (st + 2 < 16) {
+      ka[st & 1] = frag_row(stages, fo, 0, (st + 2) & 7, (st + 2) >> 3);
+      va[st & 1] = frag_row(stages, fo, 1, (st + 2) & 7, (st + 2) >> 3);
+    }
+    if (mb == 1 && (ks & 1) == 0)
+      dq_softmax_chunk<T, MASK, MASKED>(s0, d0, da0, 0, ks >> 1, sl2, l2, dd, kdiff, window, hbits);
+    MA_STEP();
+  }
+  u32x4 bk[2];
+  bk[0] = frag_col(stages, fo, 0, 0, 0);
+  MA_STEP();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int t4 = st >> 2, nb = st & 3;
+    if (st + 1 < 16) bk[(st + 1) & 1] = frag_col(stages, fo, 0, (st + 1) >> 2, (st + 1) & 3);
+    const u32x4& da = t4 < 2 ? da0[t4] : da1[t4 - 2];
+    acc[nb] = T::mma(da, bk[st & 1], acc[nb]);
+    if (st < 8 && (st & 1) == 0)
+      dq_softmax_chunk<T, MASK, MASKED>(s1, d1, da1, 1, st >> 1, sl2, l2, dd, kdiff, window, hbits);
+    MA_STEP();
+  }
+}
+
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
+                                        uint16_t* stages) {
+  constexpr int BQ = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  const int kvh = hq / a.group;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
+
+  const int qi = r0 + 32 * w + c;
+  const int qr = min(qi, a.Sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
+  const uint16_t* Op = (const uint16_t*)a.dout + (qhead * a.Sq + qr) * HD;
+  u32x4 qf[8], of[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = ld16(Qp + ks * 16 + 8 * h);
+    of[ks] = ld16(Op + ks * 16 + 8 * h);
+  }
+  const float l2 = a.lse2[qhead * sq_pad + qr];
+  const float dd = a.delta[qhead * sq_pad + qr];
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+
+  WindowSource wsrc{};
+  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  if constexpr (MASK == MASK_WINDOW) {
+    const int lo = max(0, r0 - a.window + 1);
+    const int hi = min(a.Skv, r0 + BQ);
+    const int tlo = lo >> 6, thi = (hi + 63) >> 6;
+    wsrc = WindowSource{0, 1, tlo, max(0, thi - tlo), 0};
+  } else {
+    const size_t row = qhead * a.nqb + qb;
+    bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
+  }
+  auto next = [&](int& hd, int& t, uint64_t& bits) -> bool {
+    if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
+    else return bsrc.next(hd, t, bits);
+  };
+  auto issue = [&](int t, int stg) {
+    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
+    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, w, lane);
+    tile_load_async<NW>(dst + TILE_ELEMS, Vp, t * 64, a.Skv, w, lane);
+  };
+
+  const float sl2 = a.scale_log2;
+  FragOff fo(lane);
+  constexpr int KW = 2 * tile_loads_min<NW>();   // K + V instructions per tile and wave (at least)
+  auto fetch = [&](TileRef& r) -> bool { return next(r.head, r.tile, r.bits); };
+  TileRef cur{}, nxt{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur.tile, gray_stage(0));
+  bool vnxt = vcur && fetch(nxt);
+  if (vnxt) issue(nxt.tile, gray_stage(1));
+  int it = 0;
+  // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
+  // workgroup (query rows past the end are never stored; key rows past the end always
+  // fail the window test since Sq == Skv on the window path).
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
+    else
+      return cur.bits == ~0ull;
+  };
+  auto step = [&](auto masked) -> bool {
+    constexpr bool MASKED = decltype(masked)::value;
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    TileRef n2{};
+    const bool v2 = vnxt && fetch(n2);
+    if (v2) issue(n2.tile, gray_stage(it + 2));
+    const int kdiff = qi - cur.tile * 64 - 4 * h;
+    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
+    dq_compute<T, MASK, MASKED>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits);
+    fo.advance(it);
+    ++it;
+    cur = nxt;
+    vcur = vnxt;
+    nxt = n2;
+    vnxt = v2;
+    return vcur;
+  };
+  run_tiles(vcur, step, is_full);
+
+  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
+    }
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
+  const int nbh = a.B * a.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hq, hq = bh % a.Hq;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BQ = 32 * NW;
+    // Heaviest query tiles (most visible keys) are dispatched first.
+    const int t1 = a.n_tiles - 1 - p;
+    dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
+    const int t2 = p;
+    if (a.pair && t2 != t1) {
+      __syncthreads();
+      dq_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, stages);
+    }
+  } else {
+    const int r0 = p * a.bx;
+    dq_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
+  }
+}
+
+template <class T, int MASK, int NW>
+inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+}
+
+template <class T, int MASK, int NW>
+inline void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dq_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+}
+
+// Launchers of one (element type, mask kind, waves per workgroup) variant.  Each variant is
+// compiled in an object of its own (attn_bwd_variant.hip built once per variant), so the
+// build of the large unrolled kernels runs in parallel.
+template <class T, int MASK, int NW>
+void launch_dkdv_variant(const AttnArgs& a, int grid, hipStream_t st);
+template <class T, int MASK, int NW>
+void launch_dq_variant(const AttnArgs& a, int grid, hipStream_t st);
+
+}  // namespace ma
