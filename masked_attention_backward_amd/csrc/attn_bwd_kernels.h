@@ -198,12 +198,12 @@ struct DkdvNext {
   StageLoads<NW> tiles;
   const float* lse2;
   const float* delta;
-  float* rows;
+  uint32_t rows;                 // LDS byte address of this stage's lse2 row (Delta row follows)
   int w, lane;
   __device__ __forceinline__ void issue(int i) const {
     if (i == 0) {
       if (w == 0) row_load_async(rows, lse2, lane);
-      if (w == NW - 1) row_load_async(rows + 64, delta, lane);
+      if (w == NW - 1) row_load_async(rows + 256, delta, lane);
     } else {
       tiles.issue(i - 1, w);
     }
@@ -251,16 +251,18 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   };
   // Loads of tile (hd, t) into stage `stg`: Q -> tile A, dO -> tile B, lse2/Delta rows.
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const uint32_t sld_lds = __builtin_amdgcn_readfirstlane(lds_addr(sld));
   DkdvNext<NW> nx;
   nx.w = wu;
   nx.lane = lane;
   auto prepare = [&](const TileRef& r, int stg) {
     const size_t qhead = (size_t)b * a.Hq + r.head;
     nx.tiles.prepare((const uint16_t*)a.q + qhead * a.Sq * HD, (const uint16_t*)a.dout + qhead * a.Sq * HD,
-                     stages + stg * (2 * TILE_ELEMS), r.tile * 64, a.Sq, wu, lane);
+                     stages_lds + (uint32_t)(stg * STAGE_BYTES), r.tile * 64, a.Sq, wu, lane);
     nx.lse2 = a.lse2 + qhead * sq_pad + r.tile * 64;
     nx.delta = a.delta + qhead * sq_pad + r.tile * 64;
-    nx.rows = sld + stg * 128;
+    nx.rows = sld_lds + (uint32_t)(stg * 512);
   };
   auto issue_all = [&](const TileRef& r, int stg) {
     prepare(r, stg);
@@ -356,74 +358,103 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const AttnArgs a) {
 // Workgroup = NW waves owning 32*NW consecutive query rows (wave w: rows r0+32w .. +32).
 // Per visited key tile of 64 rows, in two 32-row key blocks mb:
 //   S^T[kv][q]  = K Q^T       A = K rows (LDS),  B = Q rows (registers)
-//   dP^T[kv][q] = V dO^T      A = V rows (LDS),  B = dO rows (registers)
-//   (accumulator layout: lane column = query row, registers = key rows)
+//   dP^T[kv][q] = V dO^T      A = V rows (LDS),  B = dO rows (registers); the accumulation
+//                             starts from -Delta (the lane column is the query row, so
+//                             every register of a lane has the same Delta) and therefore
+//                             ends holding dP - Delta
 //   dQ[q][d] += dS K          A = dS (repacked accumulator), B = K columns (tr read)
-// Hand-laid stream as in dK/dV: S/dP of block 0; S/dP of block 1 + softmax of block 0;
-// dQ of block 0 + softmax of block 1; dQ of block 1.
-template <class T, int MASK, bool MASKED>
-__device__ __forceinline__ void dq_softmax_chunk(const f32x16& s, const f32x16& dp, u32x4* da, int mb, int g4,
-                                                 float sl2, float l2, float dd, int kdiff, int window,
-                                                 uint64_t hbits) {
-  float ds[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * g4 + e;
-    const int ko = mb * 32 + 8 * g4 + e;
-    float v = fast_exp2(fmaf(s[r], sl2, -l2));
-    if constexpr (MASKED) {
-      bool vis;
-      if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
-      else vis = (hbits >> ko) & 1ull;
-      v = vis ? v : 0.f;
-    }
-    ds[e] = v * (dp[r] - dd);
-  }
-  da[g4 >> 1][2 * (g4 & 1)] = T::pack2(ds[0], ds[1]);
-  da[g4 >> 1][2 * (g4 & 1) + 1] = T::pack2(ds[2], ds[3]);
+// The instruction stream of one tile is a program of 48 slots, one MFMA each:
+//   slots  0-15  S/dP of block 0     (slot 2k: S k-step k, slot 2k+1: dP k-step k)
+//   slots 16-31  S/dP of block 1
+//   slots 32-47  dQ                  (slot 32 + 4 t4 + nb: key rows 16 t4 .. +16, columns 32 nb ..)
+// Softmax rows of block 0 run one per slot from slot 17 (its first dQ slot is 32), those of
+// block 1 two per slot from slot 33 (its first dQ slot is 40).  Every operand is read from LDS
+// DQ_LA slots before its MFMA; at slot DQ_SYNC_SLOT each wave waits for its own loads of the
+// next tile and the workgroup meets at a barrier, after which the reads for the last DQ_LA
+// slots already fetch the next tile's first operands.  The global->LDS loads of the tile two
+// ahead are spread over slots 1..40.
+constexpr int DQ_LA = 4;
+constexpr int DQ_SLOTS = 48;
+constexpr int DQ_SYNC_SLOT = DQ_SLOTS - DQ_LA;
+
+__host__ __device__ constexpr int dq_row_slot(int mb, int r) { return mb == 0 ? 17 + r : 33 + r / 2; }
+
+// Is slot `s` the one that issues load instruction i of NI?
+__host__ __device__ constexpr bool dq_dma_at(int i, int ni, int s) { return (i * 40) / ni + 1 == s; }
+
+template <class T>
+struct DqCtx {
+  u32x4 qf[8], of[8];   // this lane's query row of Q and dO (B operands)
+  f32x16 acc[4];        // dQ accumulators, columns 32 nb + c
+  f32x16 negd;          // -Delta of this lane's query row in all 16 registers
+  u32x4 fr[DQ_LA];      // operand fragments in flight (carried from one tile to the next)
+};
+
+// Operand of slot s of a tile: K / V rows for S / dP, K columns for dQ.
+template <int s>
+__device__ __forceinline__ u32x4 dq_frag(const uint16_t* stages, const FragOff& fo) {
+  if constexpr (s < 32) return frag_row(stages, fo, s & 1, (s % 16) / 2, s / 16);
+  else return frag_col(stages, fo, 0, (s - 32) / 4, (s - 32) % 4);
 }
 
-// One key tile: tile A of the stage = K, tile B = V.
-template <class T, int MASK, bool MASKED>
-__device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
-                                           const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
-                                           int window, uint64_t hbits) {
-  f32x16 s0, d0, s1, d1;
-  u32x4 ka[2], va[2];
-  ka[0] = frag_row(stages, fo, 0, 0, 0);
-  va[0] = frag_row(stages, fo, 1, 0, 0);
-  ka[1] = frag_row(stages, fo, 0, 1, 0);
-  va[1] = frag_row(stages, fo, 1, 1, 0);
-  u32x4 da0[2], da1[2];
-  MA_STEP();
-#pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int mb = st >> 3, ks = st & 7;
-    f32x16& sc = mb ? s1 : s0;
-    f32x16& dc = mb ? d1 : d0;
-    sc = T::mma(ka[st & 1], qf[ks], ks ? sc : zero16());
-    dc = T::mma(va[st & 1], of[ks], ks ? dc : zero16());
-    if (st + 2 < 16) {
-      ka[st & 1] = frag_row(stages, fo, 0, (st + 2) & 7, (st + 2) >> 3);
-      va[st & 1] = frag_row(stages, fo, 1, (st + 2) & 7, (st + 2) >> 3);
+// One key tile (tile A of the stage = K, tile B = V).  `fo` addresses this tile's stage,
+// `fn` the next tile's (only its first DQ_LA row fragments are read through it).
+template <class T, int MASK, int NW, bool MASKED>
+__device__ __forceinline__ void dq_compute(DqCtx<T>& x, const FragOff& fo, const FragOff& fn,
+                                           const uint16_t* stages, float sl2, float l2, int kdiff, int window,
+                                           uint64_t hbits, const StageLoads<NW>& nx, int w) {
+  constexpr int NI = 2 * StageLoads<NW>::J;
+  constexpr int KW = 2 * tile_loads_min<NW>();
+  f32x16 sacc[2], dacc[2];    // S^T and dP^T - Delta of blocks 0 and 1
+  u32x4 da[2][2];             // dS operands: [block][k-step of 16 key rows]
+  float pk[2];                // first row of a pair, per block
+  static_for<0, DQ_SLOTS>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    // The MFMA of this slot.
+    if constexpr (s < 32) {
+      constexpr int mb = s / 16, ks = (s % 16) / 2;
+      if constexpr ((s & 1) == 0)
+        sacc[mb] = T::mma(x.fr[s % DQ_LA], x.qf[ks], ks ? sacc[mb] : zero16());
+      else
+        dacc[mb] = T::mma(x.fr[s % DQ_LA], x.of[ks], ks ? dacc[mb] : x.negd);
+    } else {
+      constexpr int j = s - 32, t4 = j / 4, nb = j % 4;
+      x.acc[nb] = T::mma(da[t4 / 2][t4 % 2], x.fr[s % DQ_LA], x.acc[nb]);
     }
-    if (mb == 1 && (ks & 1) == 0)
-      dq_softmax_chunk<T, MASK, MASKED>(s0, d0, da0, 0, ks >> 1, sl2, l2, dd, kdiff, window, hbits);
+    // Next tile's data complete in LDS (every wave's loads), previous readers done.
+    if constexpr (s == DQ_SYNC_SLOT) {
+      wait_vmcnt<KW>();
+      barrier_keep_reads();
+    }
+    // Operand read for slot s + DQ_LA (of the next tile past the end of this one).
+    if constexpr (s + DQ_LA < DQ_SLOTS) x.fr[(s + DQ_LA) % DQ_LA] = dq_frag<s + DQ_LA>(stages, fo);
+    else x.fr[(s + DQ_LA) % DQ_LA] = dq_frag<s + DQ_LA - DQ_SLOTS>(stages, fn);
+    // Softmax rows of this slot.
+    static_for<0, 2>([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (dq_row_slot(mb, r) == s) {
+          float v = fast_exp2(fmaf(sacc[mb][r], sl2, -l2));
+          if constexpr (MASKED) {
+            constexpr int ko = mb * 32 + 8 * (r / 4) + (r % 4);
+            bool vis;
+            if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
+            else vis = (hbits >> ko) & 1ull;
+            v = vis ? v : 0.f;
+          }
+          const float d = v * dacc[mb][r];
+          if constexpr ((r & 1) == 0) pk[mb] = d;
+          else da[mb][r / 8][(r % 8) / 2] = T::pack2(pk[mb], d);
+        }
+      });
+    });
+    // Global->LDS loads of the tile two ahead.
+    static_for<0, NI>([&](auto ic) {
+      if constexpr (dq_dma_at(decltype(ic)::value, NI, s)) nx.issue(decltype(ic)::value, w);
+    });
     MA_STEP();
-  }
-  u32x4 bk[2];
-  bk[0] = frag_col(stages, fo, 0, 0, 0);
-  MA_STEP();
-#pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int t4 = st >> 2, nb = st & 3;
-    if (st + 1 < 16) bk[(st + 1) & 1] = frag_col(stages, fo, 0, (st + 1) >> 2, (st + 1) & 3);
-    const u32x4& da = t4 < 2 ? da0[t4] : da1[t4 - 2];
-    acc[nb] = T::mma(da, bk[st & 1], acc[nb]);
-    if (st < 8 && (st & 1) == 0)
-      dq_softmax_chunk<T, MASK, MASKED>(s1, d1, da1, 1, st >> 1, sl2, l2, dd, kdiff, window, hbits);
-    MA_STEP();
-  }
+  });
 }
 
 template <class T, int MASK, int NW>
@@ -431,6 +462,8 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
                                         uint16_t* stages) {
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
   const size_t qhead = (size_t)b * a.Hq + hq;
   const int kvh = hq / a.group;
   const size_t kvhead = (size_t)b * a.Hkv + kvh;
@@ -438,21 +471,22 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
   const int sq_pad = (a.Sq + 63) & ~63;
 
+  DqCtx<T> x;
   const int qi = r0 + 32 * w + c;
   const int qr = min(qi, a.Sq - 1);
   const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
   const uint16_t* Op = (const uint16_t*)a.dout + (qhead * a.Sq + qr) * HD;
-  u32x4 qf[8], of[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    qf[ks] = ld16(Qp + ks * 16 + 8 * h);
-    of[ks] = ld16(Op + ks * 16 + 8 * h);
+    x.qf[ks] = ld16(Qp + ks * 16 + 8 * h);
+    x.of[ks] = ld16(Op + ks * 16 + 8 * h);
   }
   const float l2 = a.lse2[qhead * sq_pad + qr];
-  const float dd = a.delta[qhead * sq_pad + qr];
-  f32x16 acc[4];
+  const float nd = -a.delta[qhead * sq_pad + qr];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+  for (int i = 0; i < 16; ++i) x.negd[i] = nd;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) x.acc[nb] = zero16();
 
   WindowSource wsrc{};
   BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
@@ -469,51 +503,65 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(hd, t, bits);
     else return bsrc.next(hd, t, bits);
   };
-  auto issue = [&](int t, int stg) {
-    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
-    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, w, lane);
-    tile_load_async<NW>(dst + TILE_ELEMS, Vp, t * 64, a.Skv, w, lane);
+  StageLoads<NW> nx;
+  auto prepare = [&](int t, int stg) {
+    nx.prepare(Kp, Vp, stages_lds + (uint32_t)(stg * STAGE_BYTES), t * 64, a.Skv, wu, lane);
+  };
+  auto issue_all = [&](int t, int stg) {
+    prepare(t, stg);
+#pragma unroll
+    for (int i = 0; i < 2 * StageLoads<NW>::J; ++i) nx.issue(i, wu);
   };
 
   const float sl2 = a.scale_log2;
   FragOff fo(lane);
   constexpr int KW = 2 * tile_loads_min<NW>();   // K + V instructions per tile and wave (at least)
   auto fetch = [&](TileRef& r) -> bool { return next(r.head, r.tile, r.bits); };
+  // Tiles i and i + 1 are in flight when tile i is computed; tile i + 2 is issued then.
   TileRef cur{}, nxt{};
   bool vcur = fetch(cur);
-  if (vcur) issue(cur.tile, gray_stage(0));
-  bool vnxt = vcur && fetch(nxt);
-  if (vnxt) issue(nxt.tile, gray_stage(1));
-  int it = 0;
-  // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
-  // workgroup (query rows past the end are never stored; key rows past the end always
-  // fail the window test since Sq == Skv on the window path).
-  auto is_full = [&]() -> bool {
-    if constexpr (MASK == MASK_WINDOW)
-      return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
-    else
-      return cur.bits == ~0ull;
-  };
-  auto step = [&](auto masked) -> bool {
-    constexpr bool MASKED = decltype(masked)::value;
-    if (vnxt) wait_vmcnt<KW>();
+  if (vcur) {
+    issue_all(cur.tile, gray_stage(0));
+    const bool vn = fetch(nxt);
+    if (vn) issue_all(nxt.tile, gray_stage(1));
+    if (vn) wait_vmcnt<KW>();
     else wait_vmcnt<0>();
-    __syncthreads();
-    TileRef n2{};
-    const bool v2 = vnxt && fetch(n2);
-    if (v2) issue(n2.tile, gray_stage(it + 2));
-    const int kdiff = qi - cur.tile * 64 - 4 * h;
-    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
-    dq_compute<T, MASK, MASKED>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits);
-    fo.advance(it);
-    ++it;
-    cur = nxt;
-    vcur = vnxt;
-    nxt = n2;
-    vnxt = v2;
-    return vcur;
-  };
-  run_tiles(vcur, step, is_full);
+    barrier_keep_reads();
+    static_for<0, DQ_LA>([&](auto sc) { x.fr[decltype(sc)::value] = dq_frag<decltype(sc)::value>(stages, fo); });
+    bool vnxt = vn;
+    int it = 0;
+    // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
+    // workgroup (query rows past the end are never stored; key rows past the end always
+    // fail the window test since Sq == Skv on the window path).
+    auto is_full = [&]() -> bool {
+      if constexpr (MASK == MASK_WINDOW)
+        return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
+      else
+        return cur.bits == ~0ull;
+    };
+    auto step = [&](auto masked) -> bool {
+      constexpr bool MASKED = decltype(masked)::value;
+      TileRef n2{};
+      const bool v2 = vnxt && fetch(n2);
+      // Without a tile two ahead the loads repeat the current one into the free stage, which
+      // keeps the step free of branches; they are drained before the workgroup moves on.
+      prepare(v2 ? n2.tile : cur.tile, gray_stage(it + 2));
+      const int kdiff = qi - cur.tile * 64 - 4 * h;
+      const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
+      FragOff fn = fo;
+      fn.advance(it);
+      dq_compute<T, MASK, NW, MASKED>(x, fo, fn, stages, sl2, l2, kdiff, a.window, hbits, nx, wu);
+      fo = fn;
+      ++it;
+      cur = nxt;
+      const bool vc = vnxt;
+      nxt = n2;
+      vnxt = v2;
+      return vc;
+    };
+    run_tiles(true, step, is_full);
+    wait_vmcnt<0>();
+  }
 
   // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
   uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
@@ -522,7 +570,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
+      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(x.acc[nb][r] * a.scale);
     }
   }
 }
@@ -530,13 +578,32 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
-  const int nbh = a.B * a.Hq;
   const int wg = blockIdx.x;
-  const int bh = wg % nbh, p = wg / nbh;
-  const int b = bh / a.Hq, hq = bh % a.Hq;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BQ = 32 * NW;
-    // Heaviest query tiles (most visible keys) are dispatched first.
+    // Work item = (batch, query head, tile pair p).  Consecutive workgroups go to the eight
+    // XCDs in turn; when the (batch, kv head) pairs split evenly over them, XCD x serves the
+    // kv heads x, x + 8, ..., so the query heads that stream the same K/V tiles share that
+    // XCD's L2.  Lower p (heavier tiles) is dispatched first either way.
+    int b, hq, p;
+    const int nbk = a.B * a.Hkv;
+    if ((nbk & 7) == 0) {
+      const int xcd = wg & 7, idx = wg >> 3;
+      const int per = (nbk >> 3) * a.group;   // query heads served by one XCD
+      p = idx / per;
+      const int rem = idx - p * per;
+      const int m = rem / a.group, hs = rem - m * a.group;
+      const int bk = xcd + 8 * m;
+      b = bk / a.Hkv;
+      hq = (bk - b * a.Hkv) * a.group + hs;
+    } else {
+      const int nbh = a.B * a.Hq;
+      const int bh = wg % nbh;
+      p = wg / nbh;
+      b = bh / a.Hq;
+      hq = bh % a.Hq;
+    }
+    // Heaviest query tiles (most visible keys) first.
     const int t1 = a.n_tiles - 1 - p;
     dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
     const int t2 = p;
@@ -545,6 +612,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
       dq_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, stages);
     }
   } else {
+    const int nbh = a.B * a.Hq;
+    const int bh = wg % nbh, p = wg / nbh;
+    const int b = bh / a.Hq, hq = bh % a.Hq;
     const int r0 = p * a.bx;
     dq_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
   }

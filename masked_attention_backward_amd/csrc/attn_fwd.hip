@@ -23,6 +23,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
                                          uint16_t* stages) {
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
   const size_t qhead = (size_t)b * a.Hq + hq;
   const int kvh = hq / a.group;
   const size_t kvhead = (size_t)b * a.Hkv + kvh;
@@ -73,9 +75,9 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     }
   };
   auto issue = [&](int t, int stg) {
-    uint16_t* dst = stages + stg * (2 * TILE_ELEMS);
-    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, w, lane);
-    tile_load_async<NW>(dst + TILE_ELEMS, Vp, t * 64, a.Skv, w, lane);
+    const uint32_t dst = stages_lds + (uint32_t)(stg * STAGE_BYTES);
+    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, wu, lane);
+    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, a.Skv, wu, lane);
   };
 
   const float sl2 = a.scale_log2;

@@ -101,7 +101,8 @@ __device__ __forceinline__ u32x4 frag_col(const uint16_t* stages, const FragOff&
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// LDS byte address of a pointer into a __shared__ array.
+// LDS byte address of a pointer into a __shared__ array (taken once per kernel: the
+// generic-to-LDS conversion carries a null check, so the kernels keep integer addresses).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
 }
@@ -129,7 +130,7 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 // of row r fetches logical chunk p ^ f(r).  16 wave-instructions per tile, spread over
 // the NW waves of the workgroup.
 template <int NW>
-__device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* base, int row0, int nrows, int w,
+__device__ __forceinline__ void tile_load_async(uint32_t tile_lds, const uint16_t* base, int row0, int nrows, int w,
                                                 int lane) {
 #pragma unroll
   for (int j = 0; j < (16 + NW - 1) / NW; ++j) {
@@ -139,15 +140,15 @@ __device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* 
       const int p = lane & 15;
       const int g = min(row0 + row, nrows - 1);
       const uint32_t off = 2u * (uint32_t)(g * HD + ((p ^ swz(row)) << 3));
-      dma16(base, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + u * 512)));
+      dma16(base, off, __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)u * 1024u));
     }
   }
 }
 
 // 64 consecutive fp32 values straight into LDS by one wave (the per-row buffers are
 // padded to a multiple of 64 rows).
-__device__ __forceinline__ void row_load_async(float* dst, const float* src, int lane) {
-  dma4(src, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
+__device__ __forceinline__ void row_load_async(uint32_t dst_lds, const float* src, int lane) {
+  dma4(src, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane(dst_lds));
 }
 
 // The global->LDS loads of one stage (tile A and tile B of 64 rows each, same rows of two
@@ -160,14 +161,14 @@ struct StageLoads {
   static constexpr int J = (16 + NW - 1) / NW;   // instructions per tile for wave 0
   const uint16_t* srca;                          // head base of tensor A (wave-uniform)
   const uint16_t* srcb;                          // head base of tensor B
-  uint16_t* dst;                                 // LDS stage (tile A; tile B follows)
+  uint32_t dst;                                  // LDS byte address of the stage (tile A; tile B follows)
   uint32_t off[J];                               // this lane's byte offset per instruction
 
-  __device__ __forceinline__ void prepare(const uint16_t* a, const uint16_t* b, uint16_t* stage, int row0, int nrows,
-                                          int w, int lane) {
+  __device__ __forceinline__ void prepare(const uint16_t* a, const uint16_t* b, uint32_t stage_lds, int row0,
+                                          int nrows, int w, int lane) {
     srca = a;
     srcb = b;
-    dst = stage;
+    dst = stage_lds;
     const int p = lane & 15;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -180,8 +181,8 @@ struct StageLoads {
   __device__ __forceinline__ void issue(int i, int w) const {
     const int j = i < J ? i : i - J;
     if (!exists(j, w)) return;
-    uint16_t* d = dst + (i < J ? 0 : TILE_ELEMS) + (w + j * NW) * 512;
-    dma16(i < J ? srca : srcb, off[j], __builtin_amdgcn_readfirstlane(lds_addr(d)));
+    const uint32_t d = dst + (uint32_t)((i < J ? 0 : TILE_BYTES) + (w + j * NW) * 1024);
+    dma16(i < J ? srca : srcb, off[j], __builtin_amdgcn_readfirstlane(d));
   }
 };
 
@@ -190,6 +191,14 @@ struct StageLoads {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the LDS-read drain of __syncthreads: LDS reads a wave still has
+// in flight stay in flight (their results are waited for where they are used).  The empty
+// asm with a memory clobber keeps the compiler from moving LDS reads across the barrier.
+__device__ __forceinline__ void barrier_keep_reads() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Number of global->LDS instructions a wave issues for one 64 x 128 tile (the smallest over
