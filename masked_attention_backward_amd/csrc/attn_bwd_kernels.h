@@ -620,6 +620,220 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------- dQ, two workgroups per CU
+// The same products as dq_kernel (S^T = K Q^T, dP^T = V dO^T, dQ += dS K per 32-row key
+// block), written for two resident workgroups per compute unit: two LDS stages (64 KiB per
+// workgroup) and at most 256 registers per lane, so every SIMD holds two waves.  A wave
+// issues at most one instruction per issue cycle; with two waves per SIMD the LDS reads,
+// scalar work and softmax of one wave issue next to the matrix-core work of the other, and
+// each wave's waits are covered by the other one.  Per tile and key block mb: S/dP (16
+// MFMA), softmax of the block, dQ of the block (8 MFMA).
+// `masked` (uniform) selects the tiles that need the visibility test; it is applied to the
+// block's S in place (masked entries become -inf, so exp2 gives exactly 0) behind a scalar
+// branch, which keeps one loop body for all tiles.
+template <class T, int MASK>
+__device__ __forceinline__ void dq2_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
+                                            const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
+                                            int window, uint64_t hbits, bool masked) {
+  static_for<0, 2>([&](auto mc) {
+    constexpr int mb = decltype(mc)::value;
+    // S/dP of the block: 16 MFMAs, each operand read two MFMAs ahead.
+    f32x16 s, d;
+    u32x4 fa[2];
+    fa[0] = frag_row(stages, fo, 0, 0, mb);
+    fa[1] = frag_row(stages, fo, 1, 0, mb);
+    MA_STEP();
+    static_for<0, 16>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, ks = j / 2;
+      const u32x4 op = fa[j & 1];
+      if constexpr (j + 2 < 16) fa[j & 1] = frag_row(stages, fo, j & 1, (j + 2) / 2, mb);
+      if constexpr ((j & 1) == 0) s = T::mma(op, qf[ks], ks ? s : zero16());
+      else d = T::mma(op, of[ks], ks ? d : zero16());
+      MA_STEP();
+    });
+    if (masked) {
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int ko = mb * 32 + 8 * (r / 4) + (r % 4);
+        bool vis;
+        if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
+        else vis = (hbits >> ko) & 1ull;
+        s[r] = vis ? s[r] : -INFINITY;
+      });
+    }
+    MA_STEP();
+    // Softmax of the block's 16 key rows (registers), this lane's query row.
+    u32x4 da[2];
+    float pk = 0.f;
+    static_for<0, 16>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const float v = fast_exp2(fmaf(s[r], sl2, -l2));
+      const float ds = v * (d[r] - dd);
+      if constexpr ((r & 1) == 0) pk = ds;
+      else da[r / 8][(r % 8) / 2] = T::pack2(pk, ds);
+    });
+    MA_STEP();
+    // dQ of the block: 8 MFMAs, K columns read two MFMAs ahead.
+    u32x4 fb[2];
+    fb[0] = frag_col(stages, fo, 0, 2 * mb, 0);
+    fb[1] = frag_col(stages, fo, 0, 2 * mb, 1);
+    MA_STEP();
+    static_for<0, 8>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
+      const u32x4 op = fb[j & 1];
+      if constexpr (j + 2 < 8) fb[j & 1] = frag_col(stages, fo, 0, 2 * mb + (j + 2) / 4, (j + 2) % 4);
+      acc[nb] = T::mma(da[t], op, acc[nb]);
+      MA_STEP();
+    });
+  });
+}
+
+template <class T, int MASK, int NW>
+__device__ __forceinline__ void dq2_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
+                                         uint16_t* stages) {
+  constexpr int BQ = 32 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  const int kvh = hq / a.group;
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
+
+  const int qi = r0 + 32 * w + c;
+  const int qr = min(qi, a.Sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
+  const uint16_t* Op = (const uint16_t*)a.dout + (qhead * a.Sq + qr) * HD;
+  u32x4 qf[8], of[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = ld16(Qp + ks * 16 + 8 * h);
+    of[ks] = ld16(Op + ks * 16 + 8 * h);
+  }
+  const float l2 = a.lse2[qhead * sq_pad + qr];
+  const float dd = a.delta[qhead * sq_pad + qr];
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+
+  WindowSource wsrc{};
+  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  if constexpr (MASK == MASK_WINDOW) {
+    const int lo = max(0, r0 - a.window + 1);
+    const int hi = min(a.Skv, r0 + BQ);
+    const int tlo = lo >> 6, thi = (hi + 63) >> 6;
+    wsrc = WindowSource{0, 1, tlo, max(0, thi - tlo), 0};
+  } else {
+    const size_t row = qhead * a.nqb + qb;
+    bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
+  }
+  auto fetch = [&](TileRef& r) -> bool {
+    if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);
+    else return bsrc.next(r.head, r.tile, r.bits);
+  };
+  auto issue = [&](int t, int stg) {
+    const uint32_t dst = stages_lds + (uint32_t)(stg * STAGE_BYTES);
+    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, wu, lane);
+    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, a.Skv, wu, lane);
+  };
+
+  const float sl2 = a.scale_log2;
+  FragOff fo(lane);
+  TileRef cur{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur.tile, 0);
+  int it = 0;
+  // Key tiles that need no mask: every (q, kv) inside the window for all rows of the
+  // workgroup (query rows past the end are never stored; key rows past the end always
+  // fail the window test since Sq == Skv on the window path).
+  auto is_full = [&]() -> bool {
+    if constexpr (MASK == MASK_WINDOW)
+      return (r0 - (cur.tile * 64 + 63) >= 0) && (r0 + BQ - 1 - cur.tile * 64 < a.window);
+    else
+      return cur.bits == ~0ull;
+  };
+  auto step = [&]() -> bool {
+    const bool masked = !is_full();
+    // This tile's loads landed (every wave), and every wave is done with the other stage.
+    wait_vmcnt<0>();
+    __syncthreads();
+    TileRef nx{};
+    const bool vn = fetch(nx);
+    if (vn) issue(nx.tile, (it + 1) & 1);
+    const int kdiff = qi - cur.tile * 64 - 4 * h;
+    const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
+    dq2_compute<T, MASK>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits, masked);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fo.row[i] ^= STAGE_BYTES;
+      fo.col[i] ^= STAGE_BYTES;
+    }
+    ++it;
+    cur = nx;
+    return vn;
+  };
+  while (vcur) vcur = step();
+
+  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
+    }
+  }
+}
+
+// Work item decode of the window-path dQ grid (batch, query head, tile pair p): see
+// dq_kernel.
+__device__ __forceinline__ void dq_window_item(const AttnArgs& a, int wg, int& b, int& hq, int& p) {
+  const int nbk = a.B * a.Hkv;
+  if ((nbk & 7) == 0) {
+    const int xcd = wg & 7, idx = wg >> 3;
+    const int per = (nbk >> 3) * a.group;
+    p = idx / per;
+    const int rem = idx - p * per;
+    const int m = rem / a.group, hs = rem - m * a.group;
+    const int bk = xcd + 8 * m;
+    b = bk / a.Hkv;
+    hq = (bk - b * a.Hkv) * a.group + hs;
+  } else {
+    const int nbh = a.B * a.Hq;
+    const int bh = wg % nbh;
+    p = wg / nbh;
+    b = bh / a.Hq;
+    hq = bh % a.Hq;
+  }
+}
+
+template <class T, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void dq2_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[2 * 2 * TILE_ELEMS];
+  const int wg = blockIdx.x;
+  if constexpr (MASK == MASK_WINDOW) {
+    constexpr int BQ = 32 * NW;
+    int b, hq, p;
+    dq_window_item(a, wg, b, hq, p);
+    const int t1 = a.n_tiles - 1 - p;
+    dq2_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
+    const int t2 = p;
+    if (a.pair && t2 != t1) {
+      __syncthreads();
+      dq2_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, stages);
+    }
+  } else {
+    const int nbh = a.B * a.Hq;
+    const int bh = wg % nbh, p = wg / nbh;
+    const int b = bh / a.Hq, hq = bh % a.Hq;
+    const int r0 = p * a.bx;
+    dq2_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
+  }
+}
+
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
@@ -627,7 +841,10 @@ inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
 
 template <class T, int MASK, int NW>
 inline void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((dq_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+  if constexpr (MASK == MASK_WINDOW)
+    hipLaunchKernelGGL((dq2_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
 }
 
 // Launchers of one (element type, mask kind, waves per workgroup) variant.  Each variant is
