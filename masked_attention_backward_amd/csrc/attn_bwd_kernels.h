@@ -28,14 +28,21 @@ namespace ma {
 
 // ------------------------------------------------------------------ tile sources
 // Sequence of (query head, 64-row tile, row bitmask) a stationary workgroup visits.
+// Heads [head, hend) in order, each over the tiles [tlo, thi); counters only, no division.
 struct WindowSource {
-  int head0, nheads, tlo, nt, it;
-  __device__ bool next(int& head, int& tile, uint64_t& bits) {
-    if (it >= nheads * nt) return false;
-    head = head0 + it / nt;
-    tile = tlo + it % nt;
+  int head, hend, tlo, thi, tile;
+  __device__ static WindowSource make(int head0, int nheads, int tlo, int nt) {
+    return WindowSource{head0, nt > 0 ? head0 + nheads : head0, tlo, tlo + nt, tlo};
+  }
+  __device__ bool next(int& hd, int& t, uint64_t& bits) {
+    if (head >= hend) return false;
+    hd = head;
+    t = tile;
     bits = 0;
-    ++it;
+    if (++tile >= thi) {
+      tile = tlo;
+      ++head;
+    }
     return true;
   }
 };
@@ -70,11 +77,15 @@ struct BlockSource {
 // the end of the block's S/dP and the first dV/dK slot that consumes the row's k-step
 // (the row timetable below); lse2/Delta of each group of four rows are read from LDS
 // three slots before the group's first row.  The global->LDS loads of the tile two ahead
-// are spread over the slots as well.
+// are spread over the slots as well.  At slot DKDV_SYNC_SLOT every wave waits for its own
+// loads of the next tile and the workgroup meets at a barrier; the operand reads of the
+// last DKDV_LA slots then already fetch the next tile's first fragments, so consecutive
+// tiles run back to back.
 template <class T, int NW>
 struct DkdvCtx {
   u32x4 kf[8], vf[8];
   f32x16 dk[4], dv[4];
+  u32x4 fr[4];                   // operand fragments in flight (carried from one tile to the next)
 };
 
 template <int B, int E, class F>
@@ -93,36 +104,37 @@ __host__ __device__ constexpr int dkdv_row_slot(int mb, int r) {
 }
 constexpr int DKDV_LA = 4;        // LDS operand reads run this many slots ahead
 constexpr int DKDV_LD_LEAD = 3;   // lse2/Delta reads run this many slots ahead of a group
+constexpr int DKDV_SLOTS = 64;
+constexpr int DKDV_SYNC_SLOT = DKDV_SLOTS - DKDV_LA;
+
+// Operand of slot s of a tile: row fragments for S/dP, column fragments for dV/dK.
+template <int s>
+__device__ __forceinline__ u32x4 dkdv_frag(const uint16_t* stages, const FragOff& fo) {
+  if constexpr (s < 32) return frag_row(stages, fo, s & 1, (s % 16) / 2, s / 16);
+  else return frag_col(stages, fo, ((s - 32) & 1) ? 0 : 1, (s - 32) / 8, ((s - 32) % 8) / 2);
+}
 
 // Is slot `s` the one that issues load instruction i of NI (spread over the tile)?
 __host__ __device__ constexpr bool dkdv_dma_at(int i, int ni, int s) { return ((i * 32) / ni) * 2 + 1 == s; }
 
 // One tile: tile A of the stage = Q, tile B = dO.  `nx` issues the loads of the tile two
 // ahead.  `ld` points at this stage's lse2 row (64 floats) followed by its Delta row.
+// `fo` addresses this tile's stage, `fn` the next tile's (only its first DKDV_LA row
+// fragments are read through it).
 template <class T, int MASK, int NW, bool MASKED, class Next>
-__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const uint16_t* stages,
-                                             const float* ld, float sl2, int qdiff, int window, uint64_t hbits,
-                                             const Next& nx) {
+__device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& fo, const FragOff& fn,
+                                             const uint16_t* stages, const float* ld, float sl2, int qdiff,
+                                             int window, uint64_t hbits, const Next& nx) {
   constexpr int NI = Next::COUNT;
   constexpr int LA = DKDV_LA;
+  constexpr int KW = 2 * tile_loads_min<NW>();
   f32x16 sacc[2], dacc[2];       // S and dP of blocks 0 and 1
-  u32x4 fr[LA];                  // operand fragments in flight
+  u32x4* fr = x.fr;              // operand fragments in flight
   u32x4 pa[2][2], da[2][2];      // P^T and dS^T operands: [block][k-step of 16 rows]
   f32x4 Lg[2][2], Dg[2][2];      // lse2 / Delta of row groups: [block][group parity]
   float pk[2], dk2[2];           // first row of a pair, per block
 
-  // Operand of slot s: row fragments for S/dP, column fragments for dV/dK.
-  auto frag = [&](auto sc) -> u32x4 {
-    constexpr int s = decltype(sc)::value;
-    if constexpr (s < 32) return frag_row(stages, fo, s & 1, (s % 16) / 2, s / 16);
-    else {
-      constexpr int k = s - 32;
-      return frag_col(stages, fo, (k & 1) ? 0 : 1, k / 8, (k % 8) / 2);
-    }
-  };
-  static_for<0, LA>([&](auto sc) { fr[decltype(sc)::value] = frag(sc); });
-  MA_STEP();
-  static_for<0, 64>([&](auto sc) {
+  static_for<0, DKDV_SLOTS>([&](auto sc) {
     constexpr int s = decltype(sc)::value;
     // The MFMA of this slot.
     if constexpr (s < 32) {
@@ -138,8 +150,14 @@ __device__ __forceinline__ void dkdv_compute(DkdvCtx<T, NW>& x, const FragOff& f
       else
         x.dk[nb] = T::mma(da[t4 / 2][t4 % 2], fr[s % LA], x.dk[nb]);
     }
-    // Operand read for slot s + LA.
-    if constexpr (s + LA < 64) fr[(s + LA) % LA] = frag(std::integral_constant<int, s + LA>{});
+    // Next tile's data complete in LDS (every wave's loads), previous readers done.
+    if constexpr (s == DKDV_SYNC_SLOT) {
+      wait_vmcnt<KW>();
+      barrier_keep_reads();
+    }
+    // Operand read for slot s + LA (of the next tile past the end of this one).
+    if constexpr (s + LA < DKDV_SLOTS) fr[(s + LA) % LA] = dkdv_frag<s + LA>(stages, fo);
+    else fr[(s + LA) % LA] = dkdv_frag<s + LA - DKDV_SLOTS>(stages, fn);
     // lse2/Delta of a row group whose first row comes DKDV_LD_LEAD slots from now.
     static_for<0, 2>([&](auto mc) {
       constexpr int mb = decltype(mc)::value;
@@ -240,7 +258,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     const int qend = min(a.Sq, c0 + BC + a.window - 1);
     const int tlo = c0 >> 6;
     const int thi = (qend + 63) >> 6;
-    wsrc = WindowSource{kvh * a.group, a.group, tlo, max(0, thi - tlo), 0};
+    wsrc = WindowSource::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
   } else {
     const size_t row = kvhead * a.nkb + kb;
     bsrc = BlockSource{TileWalker(a.sel_k + row * a.nqb, a.cnt_k[row], a.bx, a.Sq), kvh};
@@ -281,6 +299,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   if (vcur) issue_all(cur, gray_stage(0));
   bool vnxt = vcur && fetch(nxt);
   if (vnxt) issue_all(nxt, gray_stage(1));
+  if (vcur) {
+    // First tile's data complete and visible; its first operands are read here, later
+    // tiles' at the end of the tile before them.
+    if (vnxt) wait_vmcnt<KW>();
+    else wait_vmcnt<0>();
+    barrier_keep_reads();
+    static_for<0, DKDV_LA>([&](auto sc) { x.fr[decltype(sc)::value] = dkdv_frag<decltype(sc)::value>(stages, fo); });
+  }
   int it = 0;
   // Window tiles that need no mask: every (q, kv) of the pair lies inside the window.
   // Rows past the sequence end need none either (lse2 = +inf there), nor do key columns
@@ -293,9 +319,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   };
   auto step = [&](auto masked) -> bool {
     constexpr bool MASKED = decltype(masked)::value;
-    if (vnxt) wait_vmcnt<KW>();
-    else wait_vmcnt<0>();
-    __syncthreads();
+    // Tile `cur` is complete in LDS: the barrier at the sync slot of the previous tile (or
+    // the one above for the first tile) ordered it.
     TileRef n2{};
     const bool v2 = vnxt && fetch(n2);
     // Without a tile two ahead the loads repeat the current one into the free stage, which
@@ -303,9 +328,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     prepare(v2 ? n2 : cur, gray_stage(it + 2));
     const int qdiff = cur.tile * 64 + 4 * h - kj;
     const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
-    dkdv_compute<T, MASK, NW, MASKED>(x, fo, stages, sld + gray_stage(it) * 128 + 4 * h, sl2, qdiff, a.window,
+    FragOff fn = fo;
+    fn.advance(it);
+    dkdv_compute<T, MASK, NW, MASKED>(x, fo, fn, stages, sld + gray_stage(it) * 128 + 4 * h, sl2, qdiff, a.window,
                                       hbits, nx);
-    fo.advance(it);
+    fo = fn;
     ++it;
     cur = nxt;
     vcur = vnxt;
@@ -494,7 +521,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     const int lo = max(0, r0 - a.window + 1);
     const int hi = min(a.Skv, r0 + BQ);
     const int tlo = lo >> 6, thi = (hi + 63) >> 6;
-    wsrc = WindowSource{0, 1, tlo, max(0, thi - tlo), 0};
+    wsrc = WindowSource::make(0, 1, tlo, max(0, thi - tlo));
   } else {
     const size_t row = qhead * a.nqb + qb;
     bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
@@ -724,7 +751,7 @@ __device__ __forceinline__ void dq2_tile(const AttnArgs& a, int b, int hq, int r
     const int lo = max(0, r0 - a.window + 1);
     const int hi = min(a.Skv, r0 + BQ);
     const int tlo = lo >> 6, thi = (hi + 63) >> 6;
-    wsrc = WindowSource{0, 1, tlo, max(0, thi - tlo), 0};
+    wsrc = WindowSource::make(0, 1, tlo, max(0, thi - tlo));
   } else {
     const size_t row = qhead * a.nqb + qb;
     bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
