@@ -861,9 +861,240 @@ __global__ __launch_bounds__(NW * 64, 2) void dq2_kernel(const AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------- dK / dV, two waves per SIMD
+// The same products as dkdv_kernel (S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q) for
+// the window path, written for two waves per SIMD: a workgroup of 8 waves owns 128 key rows
+// whose K and V tiles stay in LDS (64 KiB) instead of registers, next to two Q/dO stages
+// (64 KiB), which leaves at most 256 registers per lane.  Wave w works on key block w % 4
+// (32 rows) and on query half w / 4 (32 of the 64 rows) of every tile, so waves w and w + 4
+// (same SIMD) accumulate partial dK/dV of the same key rows over disjoint query rows; the
+// two partial sums are added through LDS at the end (a fixed order: bit-identical results).
+// With two waves per SIMD one wave's LDS reads, scalar work and softmax issue next to the
+// other's matrix-core work.
+constexpr int DKDV8_NW = 8;
+constexpr int DKDV8_KV_BYTES = 4 * TILE_BYTES;   // K rows 0-63, K rows 64-127, V rows 0-63, V rows 64-127
+
+template <class T, int MASK>
+__device__ __forceinline__ void dkdv8_tile(const AttnArgs& a, int b, int kvh, int c0, uint16_t* smem) {
+  constexpr int BC = 128;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int kb = wu & 3, qh = wu >> 2;
+  uint16_t* stages = smem;                                    // 2 stages x (Q tile, dO tile)
+  uint16_t* kvs = smem + 2 * 2 * TILE_ELEMS;                  // K, V of the workgroup's key rows
+  float* sld = reinterpret_cast<float*>(smem + 2 * 2 * TILE_ELEMS + 4 * TILE_ELEMS);   // 2 x (lse2, Delta)
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const uint32_t kvs_lds = __builtin_amdgcn_readfirstlane(lds_addr(kvs));
+  const uint32_t sld_lds = __builtin_amdgcn_readfirstlane(lds_addr(sld));
+  const size_t kvhead = (size_t)b * a.Hkv + kvh;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const int sq_pad = (a.Sq + 63) & ~63;
+
+  // K and V of rows [c0, c0 + 128) into LDS (rows past the end clamped; never stored).
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    tile_load_async<DKDV8_NW>(kvs_lds + (uint32_t)(t * TILE_BYTES), Kp, c0 + 64 * t, a.Skv, wu, lane);
+    tile_load_async<DKDV8_NW>(kvs_lds + (uint32_t)((2 + t) * TILE_BYTES), Vp, c0 + 64 * t, a.Skv, wu, lane);
+  }
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    dk[nb] = zero16();
+    dv[nb] = zero16();
+  }
+
+  WindowSource wsrc;
+  {
+    const int qend = min(a.Sq, c0 + BC + a.window - 1);
+    const int tlo = c0 >> 6;
+    const int thi = (qend + 63) >> 6;
+    wsrc = WindowSource::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
+  }
+  auto fetch = [&](TileRef& r) -> bool { return wsrc.next(r.head, r.tile, r.bits); };
+  StageLoads<DKDV8_NW> nx;
+  auto issue = [&](const TileRef& r, int stg) {
+    const size_t qhead = (size_t)b * a.Hq + r.head;
+    nx.prepare((const uint16_t*)a.q + qhead * a.Sq * HD, (const uint16_t*)a.dout + qhead * a.Sq * HD,
+               stages_lds + (uint32_t)(stg * STAGE_BYTES), r.tile * 64, a.Sq, wu, lane);
+#pragma unroll
+    for (int i = 0; i < 2 * StageLoads<DKDV8_NW>::J; ++i) nx.issue(i, wu);
+    const uint32_t rows = sld_lds + (uint32_t)(stg * 512);
+    if (wu == 0) row_load_async(rows, a.lse2 + qhead * sq_pad + r.tile * 64, lane);
+    if (wu == DKDV8_NW - 1) row_load_async(rows + 256, a.delta + qhead * sq_pad + r.tile * 64, lane);
+  };
+
+  const float sl2 = a.scale_log2;
+  const int kj = c0 + 32 * kb + c;
+  // Fragment offsets with the wave's blocks folded in, so every read takes a constant offset:
+  // Q/dO rows and columns of query half qh (stage folded in as well, flipped every tile), and
+  // K/V rows of key block kb (tile kb / 2, 32-row half kb % 2; V tiles follow the K tiles).
+  FragOff fo(lane);
+  FragOff fkv(lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    fo.row[i] += qh * 8192;
+    fo.col[i] += qh * 8192;
+    fkv.row[i] += (kb >> 1) * TILE_BYTES + (kb & 1) * 8192;
+  }
+  TileRef cur{};
+  bool vcur = fetch(cur);
+  if (vcur) issue(cur, 0);
+  int it = 0;
+  // Tiles where every (q, kv) of the workgroup lies inside the window need no mask (rows
+  // past the sequence end need none either: lse2 = +inf there; key columns past the end are
+  // never stored).
+  auto is_full = [&]() -> bool {
+    return (cur.tile * 64 - (c0 + BC - 1) >= 0) && (cur.tile * 64 + 63 - c0 < a.window);
+  };
+  while (vcur) {
+    const bool masked = !is_full();
+    // This tile's loads (and, first time round, K/V) landed; the other stage is free.
+    wait_vmcnt<0>();
+    __syncthreads();
+    TileRef nxr{};
+    const bool vn = fetch(nxr);
+    if (vn) issue(nxr, (it + 1) & 1);
+    const int stg = it & 1;
+    const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
+
+    // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
+    f32x16 s, d;
+    u32x4 fq[2], fk[2], fd[2], fv[2];
+    fq[0] = frag_row(stages, fo, 0, 0, 0);
+    fk[0] = frag_row(kvs, fkv, 0, 0, 0);
+    MA_STEP();
+    static_for<0, 8>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      fd[ks & 1] = frag_row(stages, fo, 1, ks, 0);
+      fv[ks & 1] = frag_row(kvs, fkv, 2, ks, 0);
+      s = T::mma(fq[ks & 1], fk[ks & 1], ks ? s : zero16());
+      MA_STEP();
+      if constexpr (ks + 1 < 8) {
+        fq[(ks + 1) & 1] = frag_row(stages, fo, 0, ks + 1, 0);
+        fk[(ks + 1) & 1] = frag_row(kvs, fkv, 0, ks + 1, 0);
+      }
+      d = T::mma(fd[ks & 1], fv[ks & 1], ks ? d : zero16());
+      MA_STEP();
+    });
+    if (masked) {
+      const int qdiff = cur.tile * 64 + qh * 32 + 4 * h - kj;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int qo = 8 * (r / 4) + (r % 4);
+        s[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s[r] : -INFINITY;
+      });
+    }
+    MA_STEP();
+    // P = exp2(S scale log2e - lse log2e), dS = P (dP - Delta); accumulator rows are query
+    // rows 8 (r / 4) + 4 h + r % 4 of this wave's half, the lane column is the key row.
+    u32x4 pa[2], da[2];
+    float pk = 0.f, dk2 = 0.f;
+    static_for<0, 4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
+      const f32x4 L = *(lds_f32x4)(ld + 8 * g);
+      const f32x4 D = *(lds_f32x4)(ld + 64 + 8 * g);
+      static_for<0, 4>([&](auto ec) {
+        constexpr int e = decltype(ec)::value, r = 4 * g + e;
+        const float v = fast_exp2(fmaf(s[r], sl2, -L[e]));
+        const float dsv = v * (d[r] - D[e]);
+        if constexpr ((r & 1) == 0) {
+          pk = v;
+          dk2 = dsv;
+        } else {
+          pa[r / 8][(r % 8) / 2] = T::pack2(pk, v);
+          da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
+        }
+      });
+    });
+    MA_STEP();
+    // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows (k-steps 2 qh, 2 qh + 1).
+    u32x4 fb[2], fc[2];
+    fb[0] = frag_col(stages, fo, 1, 0, 0);
+    fc[0] = frag_col(stages, fo, 0, 0, 0);
+    MA_STEP();
+    static_for<0, 8>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
+      if constexpr (j + 1 < 8) {
+        fb[(j + 1) & 1] = frag_col(stages, fo, 1, (j + 1) / 4, (j + 1) % 4);
+        fc[(j + 1) & 1] = frag_col(stages, fo, 0, (j + 1) / 4, (j + 1) % 4);
+      }
+      dv[nb] = T::mma(pa[t], fb[j & 1], dv[nb]);
+      MA_STEP();
+      dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
+      MA_STEP();
+    });
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fo.row[i] ^= STAGE_BYTES;
+      fo.col[i] ^= STAGE_BYTES;
+    }
+    ++it;
+    cur = nxr;
+    vcur = vn;
+  }
+  wait_vmcnt<0>();   // K/V loads when there was no tile at all
+  __syncthreads();
+
+  // Partial sums of waves w + 4 into LDS (16-byte chunks, lane-major), added by waves w.
+  f32x4* red = reinterpret_cast<f32x4*>(smem) + (size_t)kb * 32 * 64 + lane;
+  if (qh == 1) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        red[(nb * 4 + q4) * 64] = (f32x4){dk[nb][4 * q4], dk[nb][4 * q4 + 1], dk[nb][4 * q4 + 2], dk[nb][4 * q4 + 3]};
+        red[(16 + nb * 4 + q4) * 64] = (f32x4){dv[nb][4 * q4], dv[nb][4 * q4 + 1], dv[nb][4 * q4 + 2], dv[nb][4 * q4 + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
+    uint16_t* dVp = (uint16_t*)a.dv + kvhead * a.Skv * HD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 pk4 = red[(nb * 4 + q4) * 64];
+        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const int row = c0 + 32 * kb + 8 * q4 + 4 * h + e;
+          if (row < a.Skv) {
+            dKp[(size_t)row * HD + nb * 32 + c] = T::one((dk[nb][r] + pk4[e]) * a.scale);
+            dVp[(size_t)row * HD + nb * 32 + c] = T::one(dv[nb][r] + pv4[e]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class T, int MASK>
+__global__ __launch_bounds__(DKDV8_NW * 64) void dkdv8_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE_ELEMS + 4 * TILE_ELEMS + 2 * 2 * 64 * 2];
+  const int nbh = a.B * a.Hkv;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, p = wg / nbh;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  dkdv8_tile<T, MASK>(a, b, kvh, p * 128, smem);
+  const int p2 = a.n_tiles - 1 - p;
+  if (a.pair && p2 != p) {
+    __syncthreads();
+    dkdv8_tile<T, MASK>(a, b, kvh, p2 * 128, smem);
+  }
+}
+
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+  if constexpr (MASK == MASK_WINDOW)
+    hipLaunchKernelGGL((dkdv8_kernel<T, MASK>), dim3(grid), dim3(DKDV8_NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
 }
 
 template <class T, int MASK, int NW>
