@@ -47,6 +47,27 @@ struct WindowSource {
   }
 };
 
+// Tiles [tlo, thi) from the last one down, each over the heads [head0, head0 + nheads).  The
+// dK/dV workgroups of one kv head (all on one XCD) then read the same query tile at the same
+// time wherever their live ranges overlap (for causal masks they all end at the last tile).
+struct WindowSourceDesc {
+  int head0, hend, tlo, tile, head;
+  __device__ static WindowSourceDesc make(int head0, int nheads, int tlo, int nt) {
+    return WindowSourceDesc{head0, head0 + nheads, tlo, tlo + nt - 1, head0};
+  }
+  __device__ bool next(int& hd, int& t, uint64_t& bits) {
+    if (tile < tlo) return false;
+    hd = head;
+    t = tile;
+    bits = 0;
+    if (++head >= hend) {
+      head = head0;
+      --tile;
+    }
+    return true;
+  }
+};
+
 struct BlockSource {
   TileWalker walk;
   int head;
@@ -662,10 +683,13 @@ template <class T, int MASK>
 __device__ __forceinline__ void dq2_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
                                             const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
                                             int window, uint64_t hbits, bool masked) {
-  static_for<0, 2>([&](auto mc) {
+  f32x16 s[2], d[2];
+  u32x4 da[2][2];
+  float pk[2] = {0.f, 0.f};
+  // S/dP of block mb (16 MFMAs, operands read two MFMAs ahead); `extra(j)` runs after
+  // MFMA j (softmax rows of the other block).
+  auto sdp = [&](auto mc, auto&& extra) {
     constexpr int mb = decltype(mc)::value;
-    // S/dP of the block: 16 MFMAs, each operand read two MFMAs ahead.
-    f32x16 s, d;
     u32x4 fa[2];
     fa[0] = frag_row(stages, fo, 0, 0, mb);
     fa[1] = frag_row(stages, fo, 1, 0, mb);
@@ -674,8 +698,9 @@ __device__ __forceinline__ void dq2_compute(f32x16* acc, const FragOff& fo, cons
       constexpr int j = decltype(jc)::value, ks = j / 2;
       const u32x4 op = fa[j & 1];
       if constexpr (j + 2 < 16) fa[j & 1] = frag_row(stages, fo, j & 1, (j + 2) / 2, mb);
-      if constexpr ((j & 1) == 0) s = T::mma(op, qf[ks], ks ? s : zero16());
-      else d = T::mma(op, of[ks], ks ? d : zero16());
+      if constexpr ((j & 1) == 0) s[mb] = T::mma(op, qf[ks], ks ? s[mb] : zero16());
+      else d[mb] = T::mma(op, of[ks], ks ? d[mb] : zero16());
+      extra(jc);
       MA_STEP();
     });
     if (masked) {
@@ -685,22 +710,22 @@ __device__ __forceinline__ void dq2_compute(f32x16* acc, const FragOff& fo, cons
         bool vis;
         if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)window;
         else vis = (hbits >> ko) & 1ull;
-        s[r] = vis ? s[r] : -INFINITY;
+        s[mb][r] = vis ? s[mb][r] : -INFINITY;
       });
     }
     MA_STEP();
-    // Softmax of the block's 16 key rows (registers), this lane's query row.
-    u32x4 da[2];
-    float pk = 0.f;
-    static_for<0, 16>([&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      const float v = fast_exp2(fmaf(s[r], sl2, -l2));
-      const float ds = v * (d[r] - dd);
-      if constexpr ((r & 1) == 0) pk = ds;
-      else da[r / 8][(r % 8) / 2] = T::pack2(pk, ds);
-    });
-    MA_STEP();
-    // dQ of the block: 8 MFMAs, K columns read two MFMAs ahead.
+  };
+  // Softmax row r of block mb (this lane's query row, key row = register).
+  auto srow = [&](auto mc, auto rc) {
+    constexpr int mb = decltype(mc)::value, r = decltype(rc)::value;
+    const float v = fast_exp2(fmaf(s[mb][r], sl2, -l2));
+    const float ds = v * (d[mb][r] - dd);
+    if constexpr ((r & 1) == 0) pk[mb] = ds;
+    else da[mb][r / 8][(r % 8) / 2] = T::pack2(pk[mb], ds);
+  };
+  // dQ of block mb (8 MFMAs, K columns read two ahead); `extra(j)` runs after MFMA j.
+  auto dqb = [&](auto mc, auto&& extra) {
+    constexpr int mb = decltype(mc)::value;
     u32x4 fb[2];
     fb[0] = frag_col(stages, fo, 0, 2 * mb, 0);
     fb[1] = frag_col(stages, fo, 0, 2 * mb, 1);
@@ -709,10 +734,24 @@ __device__ __forceinline__ void dq2_compute(f32x16* acc, const FragOff& fo, cons
       constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
       const u32x4 op = fb[j & 1];
       if constexpr (j + 2 < 8) fb[j & 1] = frag_col(stages, fo, 0, 2 * mb + (j + 2) / 4, (j + 2) % 4);
-      acc[nb] = T::mma(da[t], op, acc[nb]);
+      acc[nb] = T::mma(da[mb][t], op, acc[nb]);
+      extra(jc);
       MA_STEP();
     });
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto none = [&](auto) {};
+  // S/dP of block 0; S/dP of block 1 with block 0's softmax (one row per MFMA); dQ of block
+  // 0 with block 1's softmax (two rows per MFMA); dQ of block 1.
+  sdp(I0{}, none);
+  sdp(I1{}, [&](auto jc) { srow(I0{}, jc); });
+  dqb(I0{}, [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    srow(I1{}, std::integral_constant<int, 2 * j>{});
+    srow(I1{}, std::integral_constant<int, 2 * j + 1>{});
   });
+  dqb(I1{}, none);
 }
 
 template <class T, int MASK, int NW>
@@ -905,12 +944,12 @@ __device__ __forceinline__ void dkdv8_tile(const AttnArgs& a, int b, int kvh, in
     dv[nb] = zero16();
   }
 
-  WindowSource wsrc;
+  WindowSourceDesc wsrc;
   {
     const int qend = min(a.Sq, c0 + BC + a.window - 1);
     const int tlo = c0 >> 6;
     const int thi = (qend + 63) >> 6;
-    wsrc = WindowSource::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
+    wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
   }
   auto fetch = [&](TileRef& r) -> bool { return wsrc.next(r.head, r.tile, r.bits); };
   StageLoads<DKDV8_NW> nx;
@@ -989,27 +1028,34 @@ __device__ __forceinline__ void dkdv8_tile(const AttnArgs& a, int b, int kvh, in
     MA_STEP();
     // P = exp2(S scale log2e - lse log2e), dS = P (dP - Delta); accumulator rows are query
     // rows 8 (r / 4) + 4 h + r % 4 of this wave's half, the lane column is the key row.
+    // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
+    // done one per MFMA between those eight MFMAs, so this wave keeps the matrix core busy
+    // while it finishes its softmax.
     u32x4 pa[2], da[2];
     float pk = 0.f, dk2 = 0.f;
-    static_for<0, 4>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
-      const f32x4 L = *(lds_f32x4)(ld + 8 * g);
-      const f32x4 D = *(lds_f32x4)(ld + 64 + 8 * g);
-      static_for<0, 4>([&](auto ec) {
-        constexpr int e = decltype(ec)::value, r = 4 * g + e;
-        const float v = fast_exp2(fmaf(s[r], sl2, -L[e]));
-        const float dsv = v * (d[r] - D[e]);
-        if constexpr ((r & 1) == 0) {
-          pk = v;
-          dk2 = dsv;
-        } else {
-          pa[r / 8][(r % 8) / 2] = T::pack2(pk, v);
-          da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
-        }
-      });
-    });
-    MA_STEP();
+    typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
+    f32x4 L[4], D[4];
+    L[0] = *(lds_f32x4)(ld);
+    D[0] = *(lds_f32x4)(ld + 64);
+    L[1] = *(lds_f32x4)(ld + 8);
+    D[1] = *(lds_f32x4)(ld + 72);
+    L[2] = *(lds_f32x4)(ld + 16);
+    D[2] = *(lds_f32x4)(ld + 80);
+    L[3] = *(lds_f32x4)(ld + 24);
+    D[3] = *(lds_f32x4)(ld + 88);
+    auto srow = [&](auto rc) {
+      constexpr int r = decltype(rc)::value, g = r / 4, e = r % 4;
+      const float v = fast_exp2(fmaf(s[r], sl2, -L[g][e]));
+      const float dsv = v * (d[r] - D[g][e]);
+      if constexpr ((r & 1) == 0) {
+        pk = v;
+        dk2 = dsv;
+      } else {
+        pa[r / 8][(r % 8) / 2] = T::pack2(pk, v);
+        da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
+      }
+    };
+    static_for<0, 8>(srow);
     // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows (k-steps 2 qh, 2 qh + 1).
     u32x4 fb[2], fc[2];
     fb[0] = frag_col(stages, fo, 1, 0, 0);
@@ -1022,8 +1068,10 @@ __device__ __forceinline__ void dkdv8_tile(const AttnArgs& a, int b, int kvh, in
         fc[(j + 1) & 1] = frag_col(stages, fo, 0, (j + 1) / 4, (j + 1) % 4);
       }
       dv[nb] = T::mma(pa[t], fb[j & 1], dv[nb]);
+      if constexpr (j < 4) srow(std::integral_constant<int, 8 + 2 * j>{});
       MA_STEP();
       dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
+      if constexpr (j < 4) srow(std::integral_constant<int, 9 + 2 * j>{});
       MA_STEP();
     });
 #pragma unroll
