@@ -30,6 +30,41 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_16BIT = 2516.6   # TFLOP/s, dense fp16/bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM = 8000.0          # GB/s
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (scaled by a copy kernel of known size), valid only for the kernel sources they were taken on.
+HBM_PROFILE = os.path.join(ROOT, "profiles", "dkdv8_kernel_large_causal_bf16_hbm.md")
+KERNEL_SOURCES = ["attn_bwd_kernels.h", "attn_bwd.hip", "attn_bwd_variant.hip", "ma_tiles.h", "ma_device.h",
+                  "ma_launch.h", "capi.hip"]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "masked_attention_backward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """Counter-measured bytes per launch of the dominant kernel, or None if they are stale."""
+    try:
+        with open(HBM_PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.split(":", 1)[0] in ("traffic-bytes-per-launch", "source-sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("source-sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic-bytes-per-launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def live_tiles_window(S, W, grid=64):
     """Count 64x64 (query-tile, key-tile) pairs holding at least one visible (i, j)."""
@@ -244,9 +279,10 @@ def main():
         "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
         "counted_tflop": round(total_flops / 1e12, 4),
         "kernels_ms": {"preprocess": round(mean(pre), 4), "dkdv": round(dkdv_ms, 4), "dq": round(mean(kdq), 4)},
-        "roofline": {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_16BIT, 4),
-                     "traffic": None},
+        "roofline": {"kernel": "dkdv8_kernel" if wl.kind == "sink" else "dkdv_kernel", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_16BIT, 4),
+                     "traffic": profiled_traffic() if wl.name == "large_causal" else None},
     }
     if not args.no_cpu_baseline:
         heads, spent, cores = cpu_baseline(wl, x, args.cpu_seconds)
