@@ -160,7 +160,6 @@ struct AttnArgs {
   float scale, scale_log2;
   int n_tiles;           // stationary tiles per head (window path)
   int pair;              // 1: workgroup p also runs tile n_tiles-1-p
-  int wg_per_head;       // workgroups per head along the stationary dimension
 };
 
 enum { MASK_WINDOW = 0, MASK_BLOCK = 1 };

@@ -193,14 +193,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier without the LDS-read drain of __syncthreads: LDS reads a wave still has
-// in flight stay in flight (their results are waited for where they are used).  The empty
-// asm with a memory clobber keeps the compiler from moving LDS reads across the barrier.
-__device__ __forceinline__ void barrier_keep_reads() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Number of global->LDS instructions a wave issues for one 64 x 128 tile (the smallest over
 // the waves of an NW-wave workgroup).
 template <int NW>
