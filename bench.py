@@ -32,7 +32,7 @@ PEAK_HBM = 8000.0          # GB/s
 
 # HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # (scaled by a copy kernel of known size), valid only for the kernel sources they were taken on.
-HBM_PROFILE = os.path.join(ROOT, "profiles", "dkdv8_kernel_large_causal_bf16_hbm.md")
+HBM_PROFILE = os.path.join(ROOT, "profiles", "dkdv_kernel_large_causal_bf16_hbm.md")
 KERNEL_SOURCES = ["attn_bwd_kernels.h", "attn_bwd.hip", "attn_bwd_variant.hip", "ma_tiles.h", "ma_device.h",
                   "ma_launch.h", "capi.hip"]
 
@@ -279,7 +279,7 @@ def main():
         "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
         "counted_tflop": round(total_flops / 1e12, 4),
         "kernels_ms": {"preprocess": round(mean(pre), 4), "dkdv": round(dkdv_ms, 4), "dq": round(mean(kdq), 4)},
-        "roofline": {"kernel": "dkdv8_kernel" if wl.kind == "sink" else "dkdv_kernel", "bound": "mfma",
+        "roofline": {"kernel": "dkdv_kernel", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_16BIT, 4),
                      "traffic": profiled_traffic() if wl.name == "large_causal" else None},
