@@ -176,6 +176,22 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     if (wu == NWV - 1) row_load_async(rows + 256, a.delta + qhead * sq_pad + r.tile * 64, lane);
   };
 
+  // Negate V in LDS once it has landed (sign bit of every 16-bit element): dP is then
+  // accumulated as Delta + dO (-V)^T = Delta - dP, starting from the staged Delta rows, and
+  // dS = P (dP - Delta) = -(P (Delta - dP)) costs no subtraction.
+  wait_vmcnt<0>();
+  __syncthreads();
+  {
+    u32x4* vt = reinterpret_cast<u32x4*>(kvs + Sh::KV_TILES * TILE_ELEMS);
+    constexpr int NCH = Sh::KV_TILES * TILE_BYTES / 16;   // 16-byte chunks of V
+    for (int ch = tid; ch < NCH; ch += NWV * 64) {
+      u32x4 x = vt[ch];
+      x ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      vt[ch] = x;
+    }
+  }
+  __syncthreads();
+
   const float sl2 = a.scale_log2;
   const int kj = c0 + 32 * kb + c;
   // Fragment offsets with the wave's blocks folded in, so every read takes a constant offset:
@@ -214,7 +230,17 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
 
     // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
+    typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
     f32x16 s, d;
+    {
+      // Delta of this wave's 32 query rows in accumulator order (register r = 4 g + e).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[4 * g + e] = D4[e];
+      }
+    }
     u32x4 fq[2], fk[2], fd[2], fv[2];
     fq[0] = frag_row(stages, fo, 0, 0, 0);
     fk[0] = frag_row(kvs, fkv, 0, 0, 0);
@@ -229,7 +255,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
         fq[(ks + 1) & 1] = frag_row(stages, fo, 0, ks + 1, 0);
         fk[(ks + 1) & 1] = frag_row(kvs, fkv, 0, ks + 1, 0);
       }
-      d = T::mma(fd[ks & 1], fv[ks & 1], ks ? d : zero16());
+      d = T::mma(fd[ks & 1], fv[ks & 1], d);
       MA_STEP();
     });
     if (masked) {
@@ -254,17 +280,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // done one per MFMA between those eight MFMAs.
     u32x4 pa[2], da[2];
     float pk = 0.f, dk2 = 0.f;
-    typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
-    f32x4 L[4], D[4];
+    f32x4 L[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      L[g] = *(lds_f32x4)(ld + 8 * g);
-      D[g] = *(lds_f32x4)(ld + 64 + 8 * g);
-    }
+    for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
     auto srow = [&](auto rc) {
       constexpr int r = decltype(rc)::value, g = r / 4, e = r % 4;
       const float v = fast_exp2(fmaf(s[r], sl2, -L[g][e]));
-      const float dsv = v * (d[r] - D[g][e]);
+      const float dsv = -(v * d[r]);
       if constexpr ((r & 1) == 0) {
         pk = v;
         dk2 = dsv;
@@ -381,6 +403,11 @@ template <class T, int MASK>
 __device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const u32x4* qf, const u32x4* of,
                                             const uint16_t* stages, float sl2, float l2, float dd, int kdiff,
                                             int window, uint64_t hbits, bool masked) {
+  // dP^T accumulates from -Delta (every register of a lane holds the same query row), so it
+  // ends holding dP - Delta.
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -dd;
   f32x16 s[2], d[2];
   u32x4 da[2][2];
   float pk[2] = {0.f, 0.f};
@@ -397,7 +424,7 @@ __device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const
       const u32x4 op = fa[j & 1];
       if constexpr (j + 2 < 16) fa[j & 1] = frag_row(stages, fo, j & 1, (j + 2) / 2, mb);
       if constexpr ((j & 1) == 0) s[mb] = T::mma(op, qf[ks], ks ? s[mb] : zero16());
-      else d[mb] = T::mma(op, of[ks], ks ? d[mb] : zero16());
+      else d[mb] = T::mma(op, of[ks], ks ? d[mb] : negd);
       extra(jc);
       MA_STEP();
     });
@@ -417,7 +444,7 @@ __device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const
   auto srow = [&](auto mc, auto rc) {
     constexpr int mb = decltype(mc)::value, r = decltype(rc)::value;
     const float v = fast_exp2(fmaf(s[mb][r], sl2, -l2));
-    const float ds = v * (d[mb][r] - dd);
+    const float ds = v * d[mb][r];
     if constexpr ((r & 1) == 0) pk[mb] = ds;
     else da[mb][r / 8][(r % 8) / 2] = T::pack2(pk[mb], ds);
   };
