@@ -95,7 +95,7 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
  * with Sp = 64*ceil(S/64) and R = align256(4*B*Hq*Sp):
  *   0:   Delta [B, Hq, Sp] fp32  (Delta_i = dO_i . O_i; readable after the call; rows >= S
  *        hold 0)
- *   R:   lse * log2(e) [B, Hq, Sp] fp32 (rows >= S hold +inf)
+ *   R:   lse * log2(e) [B, Hq, Sp] fp32 (rows >= S and rows with lse = -inf hold +inf)
  *   2R:  dsink partials [B, Hq, ceil(S/64)] fp32 */
 size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
@@ -141,7 +141,8 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
 
 /* Workspace bytes blocksparse_attn_bwd needs (0 on invalid sizes).  Layout, each
  * region starting at a 256-byte boundary, in this order:
- *   Delta [B, N, Sqp] fp32, lse * log2(e) [B, N, Sqp] fp32 (Sqp = 64*ceil(Sq/64)),
+ *   Delta [B, N, Sqp] fp32, lse * log2(e) [B, N, Sqp] fp32 (Sqp = 64*ceil(Sq/64); +inf for
+ *   padding rows and rows with lse = -inf),
  *   mask_t [B, N, nkb, nqb] u8,
  *   sel_q [B, N, nqb, nkb] i32, cnt_q [B, N, nqb] i32, sel_k [B, N, nkb, nqb] i32,
  *   cnt_k [B, N, nkb] i32. */

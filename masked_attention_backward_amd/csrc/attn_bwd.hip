@@ -8,7 +8,8 @@ namespace ma {
 // ------------------------------------------------------------------------ preprocess
 // Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]  (fp32) and lse2 = lse * log2(e), one
 // 64-row block per workgroup, into per-row buffers padded to a multiple of 64 rows: padding
-// rows get Delta = 0 and lse2 = +inf, so exp2(s - lse2) is exactly 0 there.
+// rows and rows without any visible key get lse2 = +inf (padding rows also Delta = 0), so
+// exp2(s - lse2) is exactly 0 there.
 // With a sink: part[b,h,blk] = sum_{i in blk} exp(sink_h - lse_i) * Delta_i, summed in a
 // fixed order (tree over the 64 rows).
 template <class T, bool SINK>
@@ -25,7 +26,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
   const size_t phead = ((size_t)b * H + h) * (size_t)nblk * 64;
   if (tid < 64) {
     const int row = blk * 64 + tid;
-    lse2[phead + row] = (row < S) ? lse[head + row] * LOG2E : INFINITY;
+    // Rows past the end and rows that see no key at all (lse = -inf) get +inf: exp2(s - lse2)
+    // is then exactly 0 for every s, including the -inf the kernels put on masked entries.
+    const float l = (row < S) ? lse[head + row] : -INFINITY;
+    lse2[phead + row] = (l > -INFINITY) ? l * LOG2E : INFINITY;
   }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {

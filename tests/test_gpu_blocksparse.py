@@ -99,6 +99,23 @@ def test_fwd(wl):
     assert np.all(np.abs(lg[fin] - rl[fin]) <= 1e-5 + 1e-5 * np.abs(rl[fin]))
 
 
+def test_bwd_empty_block_shares_tile():
+    """bx = 48: a query block with no kept key block shares a 64-row tile with a live one, so its
+    rows (lse = -inf) sit next to visible rows in the same dK/dV tile; they must contribute 0."""
+    wl = W.custom_blocksparse("b48x80_empty_in_tile", 1, 2, 200, 190, 48, 80, "random", density=0.4,
+                              seed_base=991)
+    x = W.make_inputs(wl)
+    x["block_mask"][0, 1, 2, :] = 0
+    x = with_oracle_forward(wl, x)
+    assert np.isneginf(x["lse"].numpy()).any()
+    dq, dk, dv = gpu_bwd(wl, x)
+    ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
+                                                wl.bx, wl.by, wl.scale)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
 def test_ragged_config_full():
     wl = W.WORKLOADS["ragged"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
