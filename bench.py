@@ -37,13 +37,26 @@ KERNEL_SOURCES = ["attn_bwd_kernels.h", "attn_bwd.hip", "attn_bwd_variant.hip", 
                   "ma_launch.h", "capi.hip"]
 
 
-def kernel_source_digest():
+def code_digest(texts):
+    """SHA-256 of source texts with // comments, trailing blanks and empty lines removed (so a
+    comment-only edit does not invalidate counters taken on the same code)."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "masked_attention_backward_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for text in texts:
+        for line in text.splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
+
+
+def kernel_source_digest():
+    texts = []
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "masked_attention_backward_amd", "csrc", f)) as fh:
+            texts.append(fh.read())
+    return code_digest(texts)
 
 
 def profiled_traffic():

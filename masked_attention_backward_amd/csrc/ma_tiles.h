@@ -26,10 +26,11 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// Staged operand tiles live in one LDS array of four stages x two tiles (A, B): tile k of
-// stage s starts at byte (2 s + k) * 16384.  Tiles are assigned to stages in Gray-code order
-// (tile i uses stage g(i) = j ^ (j >> 1) with j = i mod 4: 0, 1, 3, 2, 0, ...), so moving to the next
-// tile's stage is one XOR of the lane's offsets, alternately by 32 KiB and 64 KiB, and the
+// Staged operand tiles live in one LDS array of stages x two tiles (A, B): tile k of stage s
+// starts at byte (2 s + k) * 16384.  The backward kernels use two stages (the offsets flip by
+// 32 KiB from one tile to the next).  The forward kernel uses four, assigned in Gray-code order
+// (tile i uses stage g(i) = j ^ (j >> 1) with j = i mod 4: 0, 1, 3, 2, 0, ...), so moving to the
+// next tile's stage is one XOR of the lane's offsets, alternately by 32 KiB and 64 KiB, and the
 // loads of tile i + 2 go to a stage nobody reads any more.
 constexpr int TILE_BYTES = TILE_ELEMS * 2;     // 16384
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // 32768

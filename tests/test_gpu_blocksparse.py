@@ -70,6 +70,10 @@ SMALL = [
                          seed_base=205),
     W.custom_blocksparse("b80x48_dense", 1, 1, 250, 260, 80, 48, "dense", seed_base=206),
     W.custom_blocksparse("b64x96_random_emptyrows", 1, 2, 320, 300, 64, 96, "random", density=0.2, seed_base=207),
+    W.custom_blocksparse("b48x80_ragged_bf16", 2, 2, 290, 310, 48, 80, "ragged", dtype=torch.bfloat16,
+                         seed_base=208),
+    W.custom_blocksparse("b96x64_random_bf16", 1, 3, 260, 200, 96, 64, "random", dtype=torch.bfloat16,
+                         density=0.5, seed_base=209),
 ]
 
 
