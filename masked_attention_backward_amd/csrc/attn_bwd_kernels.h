@@ -242,18 +242,23 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       }
     }
     u32x4 fq[2], fk[2], fd[2], fv[2];
+    // Every operand is read one k-step (two MFMAs) before its MFMA.
     fq[0] = frag_row(stages, fo, 0, 0, 0);
     fk[0] = frag_row(kvs, fkv, 0, 0, 0);
+    fd[0] = frag_row(stages, fo, 1, 0, 0);
+    fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
     MA_STEP();
     static_for<0, 8>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
-      fd[ks & 1] = frag_row(stages, fo, 1, ks, 0);
-      fv[ks & 1] = frag_row(kvs, fkv, Sh::KV_TILES, ks, 0);
-      s = T::mma(fq[ks & 1], fk[ks & 1], ks ? s : zero16());
-      MA_STEP();
       if constexpr (ks + 1 < 8) {
         fq[(ks + 1) & 1] = frag_row(stages, fo, 0, ks + 1, 0);
         fk[(ks + 1) & 1] = frag_row(kvs, fkv, 0, ks + 1, 0);
+      }
+      s = T::mma(fq[ks & 1], fk[ks & 1], ks ? s : zero16());
+      MA_STEP();
+      if constexpr (ks + 1 < 8) {
+        fd[(ks + 1) & 1] = frag_row(stages, fo, 1, ks + 1, 0);
+        fv[(ks + 1) & 1] = frag_row(kvs, fkv, Sh::KV_TILES, ks + 1, 0);
       }
       d = T::mma(fd[ks & 1], fv[ks & 1], d);
       MA_STEP();
