@@ -223,9 +223,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // This tile's loads (and, first time round, K/V) landed; the other stage is free.
     wait_vmcnt<0>();
     __syncthreads();
-    TileRef nxr{};
-    const bool vn = fetch(nxr);
-    if (vn) issue(nxr, (it + 1) & 1);
     const int stg = it & 1;
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
 
@@ -242,11 +239,15 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       }
     }
     u32x4 fq[2], fk[2], fd[2], fv[2];
-    // Every operand is read one k-step (two MFMAs) before its MFMA.
+    // Every operand is read one k-step (two MFMAs) before its MFMA; the loads of the next tile
+    // are issued while the first reads are in flight.
     fq[0] = frag_row(stages, fo, 0, 0, 0);
     fk[0] = frag_row(kvs, fkv, 0, 0, 0);
     fd[0] = frag_row(stages, fo, 1, 0, 0);
     fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
+    TileRef nxr{};
+    const bool vn = fetch(nxr);
+    if (vn) issue(nxr, (it + 1) & 1);
     MA_STEP();
     static_for<0, 8>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
@@ -288,6 +289,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     f32x4 L[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
+    // First dV/dK operands, read before the softmax rows that precede their MFMAs.
+    u32x4 fb[2], fc[2];
+    fb[0] = frag_col(stages, fo, 1, 0, 0);
+    fc[0] = frag_col(stages, fo, 0, 0, 0);
     auto srow = [&](auto rc) {
       constexpr int r = decltype(rc)::value, g = r / 4, e = r % 4;
       const float v = fast_exp2(fmaf(s[r], sl2, -L[g][e]));
@@ -302,9 +307,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     };
     static_for<0, 8>(srow);
     // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows.
-    u32x4 fb[2], fc[2];
-    fb[0] = frag_col(stages, fo, 1, 0, 0);
-    fc[0] = frag_col(stages, fo, 0, 0, 0);
     MA_STEP();
     static_for<0, 8>([&](auto jc) {
       constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
