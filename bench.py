@@ -267,6 +267,22 @@ def main():
     hip.destroy(evs)
     mean = lambda v: sum(v) / len(v)  # noqa: E731
 
+    # The forward that makes O and lse (support, not part of the step): timed for reference.
+    def forward():
+        if wl.kind == "sink":
+            return api.attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
+        return api.blocksparse_attn_fwd(g["q"], g["k"], g["v"], g["block_mask"], wl.bx, wl.by, wl.scale)
+
+    forward()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(3):
+        forward()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / 3
+
     total_flops, per_head = counted_flops(wl, x.get("block_mask"))
     tflops = total_flops / (ms_per_step * 1e-3) / 1e12
     dkdv_alg = 0.8 * total_flops          # S, dP, dV, dK of the five counted GEMMs
@@ -292,6 +308,7 @@ def main():
         "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
         "counted_tflop": round(total_flops / 1e12, 4),
         "kernels_ms": {"preprocess": round(mean(pre), 4), "dkdv": round(dkdv_ms, 4), "dq": round(mean(kdq), 4)},
+        "fwd_ms_untimed_support": round(fwd_ms, 4),
         "roofline": {"kernel": "dkdv_kernel", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_16BIT, 4),

@@ -586,30 +586,6 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   }
 }
 
-// Work item decode of the window-path dQ grid (batch, query head, tile pair p).
-// Consecutive workgroups go to the eight XCDs in turn; when the (batch, kv head) pairs split
-// evenly over them, XCD x serves the kv heads x, x + 8, ..., so the query heads that stream
-// the same K/V tiles share that XCD's L2.  Lower p (heavier tiles) is dispatched first.
-__device__ __forceinline__ void dq_window_item(const AttnArgs& a, int wg, int& b, int& hq, int& p) {
-  const int nbk = a.B * a.Hkv;
-  if ((nbk & 7) == 0) {
-    const int xcd = wg & 7, idx = wg >> 3;
-    const int per = (nbk >> 3) * a.group;
-    p = idx / per;
-    const int rem = idx - p * per;
-    const int m = rem / a.group, hs = rem - m * a.group;
-    const int bk = xcd + 8 * m;
-    b = bk / a.Hkv;
-    hq = (bk - b * a.Hkv) * a.group + hs;
-  } else {
-    const int nbh = a.B * a.Hq;
-    const int bh = wg % nbh;
-    p = wg / nbh;
-    b = bh / a.Hq;
-    hq = bh % a.Hq;
-  }
-}
-
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stages[2 * 2 * TILE_ELEMS];
@@ -617,7 +593,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BQ = 32 * NW;
     int b, hq, p;
-    dq_window_item(a, wg, b, hq, p);
+    window_q_item(a, wg, b, hq, p);
     const int t1 = a.n_tiles - 1 - p;
     dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
     const int t2 = p;

@@ -8,7 +8,9 @@
 // accumulates.  lse = m + log(l) therefore includes the sink, and a row that sees
 // nothing ends with O = 0, lse = -inf.
 //
-// Workgroup = NW waves owning 32*NW query rows; per 64-row key tile:
+// Workgroup = NW waves owning 32*NW query rows, two workgroups per compute unit (two LDS
+// stages of K/V tiles, 64 KiB; at most 256 registers per lane, so each SIMD holds two waves
+// and one wave's softmax issues next to the other's MFMAs); per 64-row key tile:
 //   S^T[kv][q] = K Q^T      A = K rows (LDS), B = Q rows (registers); lane column = query
 //   O^T[d][q] += V^T P^T    A = V columns (tr read), B = P^T (repacked accumulator)
 // Accumulating O transposed keeps each lane's registers on its own query row, so the
@@ -82,13 +84,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 
   const float sl2 = a.scale_log2;
   FragOff fo(lane);
-  constexpr int KW = 2 * tile_loads_min<NW>();
   auto fetch = [&](TileRef& r) -> bool { return next(r.tile, r.bits); };
-  TileRef cur{}, nxt{};
+  TileRef cur{};
   bool vcur = fetch(cur);
-  if (vcur) issue(cur.tile, gray_stage(0));
-  bool vnxt = vcur && fetch(nxt);
-  if (vnxt) issue(nxt.tile, gray_stage(1));
+  if (vcur) issue(cur.tile, 0);
   int itx = 0;
   auto is_full = [&]() -> bool {
     if constexpr (MASK == MASK_WINDOW)
@@ -96,16 +95,16 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     else
       return cur.bits == ~0ull;
   };
-  auto step = [&](auto masked) -> bool {
-    constexpr bool MASKED = decltype(masked)::value;
+  auto step = [&]() -> bool {
+    const bool masked = !is_full();
     const int t = cur.tile;
     const uint64_t bits = cur.bits;
-    if (vnxt) wait_vmcnt<KW>();
-    else wait_vmcnt<0>();
+    // This tile's loads landed (every wave), and every wave is done with the other stage.
+    wait_vmcnt<0>();
     __syncthreads();
     TileRef n2{};
-    const bool v2 = vnxt && fetch(n2);
-    if (v2) issue(n2.tile, gray_stage(itx + 2));
+    const bool v2 = fetch(n2);
+    if (v2) issue(n2.tile, (itx + 1) & 1);
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -115,20 +114,28 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     }
     const int kdiff = qi - t * 64 - 4 * h;
     const uint64_t hbits = h ? (bits >> 4) : bits;
-    // Scaled logits in the log2 domain; hidden entries become -inf.
+    // Hidden entries become -inf, only on tiles that need the test (a uniform branch, which
+    // keeps one loop body for all tiles).
+    if (masked) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = mb * 32 + 8 * (r >> 2) + (r & 3);
+          bool vis;
+          if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)a.window;
+          else vis = (hbits >> ko) & 1ull;
+          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+        }
+      }
+    }
+    // Scaled logits in the log2 domain.
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ko = mb * 32 + 8 * (r >> 2) + (r & 3);
-        float x = s[mb][r] * sl2;
-        if constexpr (MASKED) {
-          bool vis;
-          if constexpr (MASK == MASK_WINDOW) vis = (unsigned)(kdiff - ko) < (unsigned)a.window;
-          else vis = (hbits >> ko) & 1ull;
-          x = vis ? x : -INFINITY;
-        }
+        const float x = s[mb][r] * sl2;
         s[mb][r] = x;
         mx = fmaxf(mx, x);
       }
@@ -160,15 +167,16 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(frag_col(stages, fo, 1, t4, nb), pb, acc[nb]);
     }
-    fo.advance(itx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fo.row[i] ^= STAGE_BYTES;
+      fo.col[i] ^= STAGE_BYTES;
+    }
     ++itx;
-    cur = nxt;
-    vcur = vnxt;
-    nxt = n2;
-    vnxt = v2;
-    return vcur;
+    cur = n2;
+    return v2;
   };
-  run_tiles(vcur, step, is_full);
+  while (vcur) vcur = step();
 
   // Epilogue: lane (c, h) holds O^T[d = nb*32 + 8(r/4) + 4h + r%4][q = qi].
   if (qi < q_end) {
@@ -189,17 +197,25 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
 }
 
 template <class T, int MASK, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[NSTAGES * 2 * TILE_ELEMS];
-  const int nbh = a.B * a.Hq;
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[2 * 2 * TILE_ELEMS];
   const int wg = blockIdx.x;
-  const int bh = wg % nbh, p = wg / nbh;
-  const int b = bh / a.Hq, hq = bh % a.Hq;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BQ = 32 * NW;
+    int b, hq, p;
+    window_q_item(a, wg, b, hq, p);
+    // Heaviest query tiles first; with `pair`, tile p also runs tile n - 1 - p.
     const int t1 = a.n_tiles - 1 - p;
     fwd_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
+    const int t2 = p;
+    if (a.pair && t2 != t1) {
+      __syncthreads();
+      fwd_tile<T, MASK, NW>(a, b, hq, t2 * BQ, a.Sq, 0, stages);
+    }
   } else {
+    const int nbh = a.B * a.Hq;
+    const int bh = wg % nbh, p = wg / nbh;
+    const int b = bh / a.Hq, hq = bh % a.Hq;
     const int r0 = p * a.bx;
     fwd_tile<T, MASK, NW>(a, b, hq, r0, min(r0 + a.bx, a.Sq), p, stages);
   }
@@ -208,9 +224,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const AttnArgs a) {
 template <class T>
 static void launch_fwd_t(const AttnArgs& a, int mask, hipStream_t st) {
   if (mask == MASK_WINDOW) {
+    // Query tiles of 128 rows; for wide windows tile p is paired with tile n - 1 - p (equal
+    // work) whenever that still leaves at least one workgroup per compute unit.
     AttnArgs w = a;
     w.n_tiles = (a.Sq + 127) / 128;
-    hipLaunchKernelGGL((fwd_kernel<T, MASK_WINDOW, 4>), dim3(a.B * a.Hq * w.n_tiles), dim3(256), 0, st, w);
+    const bool wide = a.window >= 256 && a.window * 4 >= a.Skv;
+    w.pair = (wide && a.B * a.Hq * ((w.n_tiles + 1) / 2) >= 256) ? 1 : 0;
+    const int g = a.B * a.Hq * (w.pair ? (w.n_tiles + 1) / 2 : w.n_tiles);
+    hipLaunchKernelGGL((fwd_kernel<T, MASK_WINDOW, 4>), dim3(g), dim3(256), 0, st, w);
     return;
   }
   const int g = a.B * a.Hq * a.nqb;

@@ -26,20 +26,11 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// Staged operand tiles live in one LDS array of stages x two tiles (A, B): tile k of stage s
-// starts at byte (2 s + k) * 16384.  The backward kernels use two stages (the offsets flip by
-// 32 KiB from one tile to the next).  The forward kernel uses four, assigned in Gray-code order
-// (tile i uses stage g(i) = j ^ (j >> 1) with j = i mod 4: 0, 1, 3, 2, 0, ...), so moving to the
-// next tile's stage is one XOR of the lane's offsets, alternately by 32 KiB and 64 KiB, and the
-// loads of tile i + 2 go to a stage nobody reads any more.
+// Staged operand tiles live in one LDS array of two stages x two tiles (A, B): tile k of
+// stage s starts at byte (2 s + k) * 16384; moving to the other stage flips the lane's
+// offsets by 32 KiB.
 constexpr int TILE_BYTES = TILE_ELEMS * 2;     // 16384
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // 32768
-constexpr int NSTAGES = 4;
-
-__device__ __forceinline__ int gray_stage(int i) {
-  const int j = i & 3;
-  return j ^ (j >> 1);
-}
 
 // Lane-dependent byte offsets of the MFMA operand fragments inside the staged tiles, with
 // the current stage folded in.  Every fragment read is one of these offsets plus a
@@ -65,15 +56,6 @@ struct FragOff {
     for (int nb = 0; nb < 4; ++nb) {
       col[2 * nb] = 2 * tile_off(4 * h + rin, 32 * nb + cs);
       col[2 * nb + 1] = 2 * tile_off(8 + 4 * h + rin, 32 * nb + cs);
-    }
-  }
-  // Move from the stage of tile `it` to the stage of tile it + 1.
-  __device__ __forceinline__ void advance(int it) {
-    const int x = (it & 1) ? 2 * STAGE_BYTES : STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      row[i] ^= x;
-      col[i] ^= x;
     }
   }
 };
@@ -194,50 +176,39 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Number of global->LDS instructions a wave issues for one 64 x 128 tile (the smallest over
-// the waves of an NW-wave workgroup).
-template <int NW>
-constexpr int tile_loads_min() {
-  return 16 / NW;
-}
 
 struct TileRef {
   int head, tile;
   uint64_t bits;
 };
 
-// Visibility of the elements of one (query-tile, key-tile) pair.
-//   window:  query i sees key j iff 0 <= i - j < window, both inside their sequences
-//   block:   a 64-bit mask over the 64 rows of the iterated tile (built by TileWalker)
-struct WindowVis {
-  int sq, skv, window;
-  // true when every (i, j) in [q0, q0+nq) x [k0, k0+nk) is visible
-  __device__ __forceinline__ bool full(int q0, int nq, int k0, int nk) const {
-    return (q0 - (k0 + nk - 1) >= 0) && ((q0 + nq - 1) - k0 < window) && (q0 + nq <= sq) && (k0 + nk <= skv);
+
+// Work item decode of a window-path grid over (batch, query head, tile pair p) (dQ and the
+// forward).
+// Consecutive workgroups go to the eight XCDs in turn; when the (batch, kv head) pairs split
+// evenly over them, XCD x serves the kv heads x, x + 8, ..., so the query heads that stream
+// the same K/V tiles share that XCD's L2.  Lower p (heavier tiles) is dispatched first.
+__device__ __forceinline__ void window_q_item(const AttnArgs& a, int wg, int& b, int& hq, int& p) {
+  const int nbk = a.B * a.Hkv;
+  if ((nbk & 7) == 0) {
+    const int xcd = wg & 7, idx = wg >> 3;
+    const int per = (nbk >> 3) * a.group;
+    p = idx / per;
+    const int rem = idx - p * per;
+    const int m = rem / a.group, hs = rem - m * a.group;
+    const int bk = xcd + 8 * m;
+    b = bk / a.Hkv;
+    hq = (bk - b * a.Hkv) * a.group + hs;
+  } else {
+    const int nbh = a.B * a.Hq;
+    const int bh = wg % nbh;
+    p = wg / nbh;
+    b = bh / a.Hq;
+    hq = bh % a.Hq;
   }
-  __device__ __forceinline__ bool vis(int i, int j) const {
-    return ((unsigned)(i - j) < (unsigned)window) && (i < sq) && (j < skv);
-  }
-};
+}
 
 #define MA_STEP() __builtin_amdgcn_sched_barrier(0)
 
-// Runs `step<MASKED>()` over a tile sequence, switching between the masked and the
-// unmasked variant only between runs of tiles, so each inner loop body is branch-free
-// (one basic block per variant; the accumulators never cross a branch join inside it).
-template <class Step, class IsFull>
-__device__ __forceinline__ void run_tiles(bool have, Step&& step, IsFull&& is_full) {
-  while (have) {
-    if (is_full()) {
-      do {
-        have = step(std::integral_constant<bool, false>{});
-      } while (have && is_full());
-    } else {
-      do {
-        have = step(std::integral_constant<bool, true>{});
-      } while (have && !is_full());
-    }
-  }
-}
 
 }  // namespace ma
