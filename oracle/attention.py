@@ -269,56 +269,68 @@ def sink_attention_backward_sampled(q, k, v, o, do, lse, sink, window, scale, q_
     return {"dq": dq, "dk": dk, "dv": dv, "dsink": dsink, "delta": delta}
 
 
-# ------------------------------------------------------------ path B: block-sparse MHA
+# ------------------------------------------------------------ path B: block-sparse attention
+# MHA as on the block-sparse page; with fewer K/V heads than query heads (GQA, Hq % Hkv == 0)
+# the grouping of path A applies: query head n reads K/V head n // (Hq // Hkv), the block mask
+# is per query head, and dK/dV of a K/V head sum over its group.
 
 def _block_fn(mask_bn, bx, by):
     return lambda rows, cols: block_visibility(mask_bn, bx, by, rows, cols)
 
 
 def blocksparse_attention_forward(q, k, v, block_mask, bx, by, scale):
-    """O [B,N,Sq,D] and lse [B,N,Sq] for block-sparse MHA (no sink; empty rows: O=0, lse=-inf)."""
+    """O [B,N,Sq,D] and lse [B,N,Sq] for block-sparse attention (no sink; empty rows: O=0,
+    lse=-inf).  k, v: [B,Nkv,Skv,D] with N % Nkv == 0."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     m = _u8(block_mask)
     b_, n_, sq, d = q.shape
+    g = n_ // k.shape[1]
     o = np.zeros((b_, n_, sq, d))
     lse = np.zeros((b_, n_, sq))
     for b in range(b_):
         for n in range(n_):
-            o[b, n], lse[b, n] = _head_forward(q[b, n], k[b, n], v[b, n], -np.inf, _block_fn(m[b, n], bx, by), scale)
+            o[b, n], lse[b, n] = _head_forward(q[b, n], k[b, n // g], v[b, n // g], -np.inf,
+                                               _block_fn(m[b, n], bx, by), scale)
     return o, lse
 
 
 def blocksparse_attention_backward(q, k, v, o, do, lse, block_mask, bx, by, scale):
-    """dq, dk, dv, delta for block-sparse MHA from the stored forward quantities."""
+    """dq, dk, dv, delta for block-sparse attention from the stored forward quantities."""
     q, k, v, o, do, lse = (_f64(x) for x in (q, k, v, o, do, lse))
     m = _u8(block_mask)
     b_, n_, sq, d = q.shape
+    g = n_ // k.shape[1]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     delta = np.zeros((b_, n_, sq))
     for b in range(b_):
         for n in range(n_):
-            dq[b, n], dk[b, n], dv[b, n], delta[b, n] = _head_backward(
-                q[b, n], k[b, n], v[b, n], o[b, n], do[b, n], lse[b, n], _block_fn(m[b, n], bx, by), scale)
+            dq[b, n], dk_h, dv_h, delta[b, n] = _head_backward(
+                q[b, n], k[b, n // g], v[b, n // g], o[b, n], do[b, n], lse[b, n], _block_fn(m[b, n], bx, by), scale)
+            dk[b, n // g] += dk_h
+            dv[b, n // g] += dv_h
     return {"dq": dq, "dk": dk, "dv": dv, "delta": delta}
 
 
 def blocksparse_attention_backward_sampled(q, k, v, o, do, lse, block_mask, bx, by, scale, q_rows, kv_rows):
-    """Block-sparse backward at chosen outputs: q_rows of (b, n, i), kv_rows of (b, n, j)."""
+    """Block-sparse backward at chosen outputs: q_rows of (b, n, i) -> dq[b, n, i, :], kv_rows of
+    (b, nkv, j) -> dk[b, nkv, j, :], dv[b, nkv, j, :]."""
     q, k, v, o, do, lse = (_f64(x) for x in (q, k, v, o, do, lse))
     m = _u8(block_mask)
     d = q.shape[-1]
+    g = q.shape[1] // k.shape[1]
     dq = np.zeros((len(q_rows), d))
     for t, (b, n, i) in enumerate(q_rows):
-        dq_r, _, _, _, _ = _head_backward_rows(q[b, n], k[b, n], v[b, n], o[b, n], do[b, n], lse[b, n],
+        dq_r, _, _, _, _ = _head_backward_rows(q[b, n], k[b, n // g], v[b, n // g], o[b, n], do[b, n], lse[b, n],
                                                _block_fn(m[b, n], bx, by), scale, np.array([i]))
         dq[t] = dq_r[0]
     dk = np.zeros((len(kv_rows), d))
     dv = np.zeros((len(kv_rows), d))
-    for t, (b, n, j) in enumerate(kv_rows):
-        dk_r, dv_r = _head_backward_cols(q[b, n], k[b, n], v[b, n], o[b, n], do[b, n], lse[b, n],
-                                         _block_fn(m[b, n], bx, by), scale, np.array([j]))
-        dk[t] = dk_r[0]
-        dv[t] = dv_r[0]
+    for t, (b, nkv, j) in enumerate(kv_rows):
+        for n in range(nkv * g, (nkv + 1) * g):
+            dk_r, dv_r = _head_backward_cols(q[b, n], k[b, nkv], v[b, nkv], o[b, n], do[b, n], lse[b, n],
+                                             _block_fn(m[b, n], bx, by), scale, np.array([j]))
+            dk[t] += dk_r[0]
+            dv[t] += dv_r[0]
     return {"dq": dq, "dk": dk, "dv": dv}

@@ -164,6 +164,39 @@ def test_sdpa_blocksparse_reduction(pattern):
         assert np.max(np.abs(a - b)) < 1e-12 * max(1.0, np.max(np.abs(b)))
 
 
+def test_sdpa_blocksparse_gqa_reduction():
+    """GQA block-sparse (per-query-head block mask, K/V shared by groups of query heads) equals
+    SDPA on repeated K/V with the token-expanded mask, dK/dV summed over each group."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, Sq, Skv, D, bx, by = 2, 6, 2, 40, 37, 16, 16, 8
+    g_ = Hq // Hkv
+    scale = 0.25
+    nqb, nkb = -(-Sq // bx), -(-Skv // by)
+    mask = (rng.random((B, Hq, nqb, nkb)) < 0.5).astype(np.uint8)
+    mask[..., 1] = 1   # no empty rows (SDPA would give NaN there)
+    q, do = _rand(rng, B, Hq, Sq, D), _rand(rng, B, Hq, Sq, D)
+    k, v = _rand(rng, B, Hkv, Skv, D), _rand(rng, B, Hkv, Skv, D)
+    o, lse = oracle.blocksparse_attention_forward(q, k, v, mask, bx, by, scale)
+    g = oracle.blocksparse_attention_backward(q, k, v, o, do, lse, mask, bx, by, scale)
+    tm = torch.tensor(mask, dtype=torch.bool)
+    tok = tm.repeat_interleave(bx, dim=2)[:, :, :Sq].repeat_interleave(by, dim=3)[:, :, :, :Skv]
+    kr, vr = np.repeat(k, g_, axis=1), np.repeat(v, g_, axis=1)
+    ro, rdq, rdk, rdv = _sdpa_grads(q, kr, vr, do, scale, attn_mask=tok)
+    rdk = rdk.reshape(B, Hkv, g_, Skv, D).sum(axis=2)
+    rdv = rdv.reshape(B, Hkv, g_, Skv, D).sum(axis=2)
+    for a, b in zip((o, g["dq"], g["dk"], g["dv"]), (ro, rdq, rdk, rdv)):
+        assert np.max(np.abs(a - b)) < 1e-12 * max(1.0, np.max(np.abs(b)))
+    # the sampled form returns the same rows
+    qs = [(1, 4, 0), (0, 5, 39), (1, 0, 17)]
+    ks = [(0, 1, 0), (1, 0, 36), (1, 1, 20)]
+    sm = oracle.blocksparse_attention_backward_sampled(q, k, v, o, do, lse, mask, bx, by, scale, qs, ks)
+    for t, (b, n, i) in enumerate(qs):
+        assert np.max(np.abs(sm["dq"][t] - g["dq"][b, n, i])) < 1e-12
+    for t, (b, n, j) in enumerate(ks):
+        assert np.max(np.abs(sm["dk"][t] - g["dk"][b, n, j])) < 1e-12
+        assert np.max(np.abs(sm["dv"][t] - g["dv"][b, n, j])) < 1e-12
+
+
 # ------------------------------------------------------------ augmented-key sink formulation
 
 def test_augmented_key_sink_lse_and_dsink():
