@@ -166,6 +166,29 @@ int blocksparse_attn_bwd(const void* q, const void* k, const void* v,
                          int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * (B') Block-sparse attention with grouped K/V heads (GQA).  The block-sparse page is MHA;
+ * these apply the sink page's grouping (contiguous groups: query head h reads K/V head
+ * h / (Hq / Hkv)) to it, with the block mask per query head:
+ *   q, o, dout [B, Hq, Sq, D];  k, v [B, Hkv, Skv, D];  lse [B, Hq, Sq] fp32
+ *   block_mask [B, Hq, ceil(Sq/bx), ceil(Skv/by)] uint8
+ *   dq [B, Hq, Sq, D], dk/dv [B, Hkv, Skv, D] (out; dK/dV summed over the group)
+ * Workspace: blocksparse_attn_bwd_workspace_bytes(B, Hq, Sq, Skv, D, bx, by), same layout.
+ * Errors as blocksparse_attn_fwd / blocksparse_attn_bwd, plus MA_EINVAL when Hkv < 1 or
+ * Hq % Hkv != 0.  With Hkv = Hq they are blocksparse_attn_fwd / blocksparse_attn_bwd.
+ * --------------------------------------------------------------------------------- */
+int blocksparse_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                             void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             int B, int Hq, int Hkv, int Sq, int Skv, int D, int bx, int by, float scale,
+                             int dtype, void* stream);
+int blocksparse_attn_bwd_gqa(const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             const uint8_t* block_mask,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             int B, int Hq, int Hkv, int Sq, int Skv, int D, int bx, int by, float scale,
+                             int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Profiling variants: identical work and results to attn_sink_bwd / blocksparse_attn_bwd,
  * and additionally record caller-created HIP events (hipEvent_t, passed as void*) on
  * `stream` between the stages, so per-stage device time can be read with

@@ -29,6 +29,8 @@ EXPORTS = (
     "blocksparse_attn_bwd",
     "attn_sink_bwd_timed",
     "blocksparse_attn_bwd_timed",
+    "blocksparse_attn_fwd_gqa",
+    "blocksparse_attn_bwd_gqa",
 )
 
 
@@ -64,6 +66,10 @@ def _load():
     lib.attn_sink_bwd_timed.restype = I
     lib.blocksparse_attn_bwd_timed.argtypes = lib.blocksparse_attn_bwd.argtypes + [P]
     lib.blocksparse_attn_bwd_timed.restype = I
+    lib.blocksparse_attn_fwd_gqa.argtypes = [P, P, P, P, P, P, P, Z] + [I] * 8 + [F, I, P]
+    lib.blocksparse_attn_fwd_gqa.restype = I
+    lib.blocksparse_attn_bwd_gqa.argtypes = [P] * 10 + [P, Z] + [I] * 8 + [F, I, P]
+    lib.blocksparse_attn_bwd_gqa.restype = I
     return lib
 
 
@@ -185,38 +191,44 @@ def blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D=128):
 
 def _block_shapes(q, k, block_mask, bx, by):
     B, N, Sq, D = q.shape
-    Skv = k.shape[2]
+    Nkv, Skv = k.shape[1], k.shape[2]
     nqb, nkb = -(-Sq // bx), -(-Skv // by)
     _need(block_mask, "block_mask", (B, N, nqb, nkb), torch.uint8, q.device)
-    return B, N, Sq, Skv, D
+    return B, N, Nkv, Sq, Skv, D
 
 
 def blocksparse_attn_fwd(q, k, v, block_mask, bx, by, scale=None, workspace=None):
-    """Block-sparse forward. q [B,N,Sq,128], k/v [B,N,Skv,128] -> (o, lse); empty rows: o=0, lse=-inf."""
-    B, N, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
+    """Block-sparse forward. q [B,N,Sq,128], k/v [B,Nkv,Skv,128] (N % Nkv == 0; Nkv < N groups
+    the query heads as GQA) -> (o, lse); empty rows: o=0, lse=-inf."""
+    B, N, Nkv, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
     dev = q.device
     _need(q, "q", (B, N, Sq, D), q.dtype, dev)
-    _need(k, "k", (B, N, Skv, D), q.dtype, dev)
-    _need(v, "v", (B, N, Skv, D), q.dtype, dev)
+    _need(k, "k", (B, Nkv, Skv, D), q.dtype, dev)
+    _need(v, "v", (B, Nkv, Skv, D), q.dtype, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev) if workspace is None \
         else workspace
     o = torch.empty_like(q)
     lse = torch.empty((B, N, Sq), dtype=torch.float32, device=dev)
-    st = lib.blocksparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(o), _ptr(lse), _ptr(ws),
-                                  ws.numel(), B, N, Sq, Skv, D, bx, by, scale, _dtype_code(q), _stream(dev))
+    if Nkv == N:
+        st = lib.blocksparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(o), _ptr(lse), _ptr(ws),
+                                      ws.numel(), B, N, Sq, Skv, D, bx, by, scale, _dtype_code(q), _stream(dev))
+    else:
+        st = lib.blocksparse_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(o), _ptr(lse),
+                                          _ptr(ws), ws.numel(), B, N, Nkv, Sq, Skv, D, bx, by, scale, _dtype_code(q),
+                                          _stream(dev))
     _check("blocksparse_attn_fwd", st)
     return o, lse
 
 
 def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, workspace=None):
-    """Block-sparse backward -> (dq, dk, dv)."""
-    B, N, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
+    """Block-sparse backward -> (dq, dk, dv); k/v (and dk/dv) may have fewer heads (GQA)."""
+    B, N, Nkv, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
     dev = q.device
     for name, t in (("q", q), ("o", o), ("do", do)):
         _need(t, name, (B, N, Sq, D), q.dtype, dev)
-    _need(k, "k", (B, N, Skv, D), q.dtype, dev)
-    _need(v, "v", (B, N, Skv, D), q.dtype, dev)
+    _need(k, "k", (B, Nkv, Skv, D), q.dtype, dev)
+    _need(v, "v", (B, Nkv, Skv, D), q.dtype, dev)
     _need(lse, "lse", (B, N, Sq), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev) if workspace is None \
@@ -224,8 +236,13 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    st = lib.blocksparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(block_mask),
-                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, N, Sq, Skv, D, bx, by, scale,
-                                  _dtype_code(q), _stream(dev))
+    if Nkv == N:
+        st = lib.blocksparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(block_mask),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, N, Sq, Skv, D, bx, by,
+                                      scale, _dtype_code(q), _stream(dev))
+    else:
+        st = lib.blocksparse_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(block_mask),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, N, Nkv, Sq, Skv, D,
+                                          bx, by, scale, _dtype_code(q), _stream(dev))
     _check("blocksparse_attn_bwd", st)
     return dq, dk, dv

@@ -81,6 +81,43 @@ struct BlockSource {
   }
 };
 
+// The query tiles a key block of a K/V head sees on the block path: the rows of the kv-major
+// table of every query head of its group, one head after the other (a single head for MHA).
+struct BlockGroupSource {
+  const int* sel_k = nullptr;   // [B, Hq, nkb, nqb]
+  const int* cnt_k = nullptr;   // [B, Hq, nkb]
+  size_t row0 = 0;              // (b * Hq) * nkb + kblock: table row of query head 0
+  int nkb = 0, nqb = 0, bx = 1, sq = 1;
+  int head = 0, hend = 0;
+  TileWalker walk{nullptr, 0, 1, 1};
+  __device__ void init(const AttnArgs& a, int b, int kvh, int kblock) {
+    sel_k = a.sel_k;
+    cnt_k = a.cnt_k;
+    row0 = (size_t)b * a.Hq * a.nkb + kblock;
+    nkb = a.nkb;
+    nqb = a.nqb;
+    bx = a.bx;
+    sq = a.Sq;
+    head = kvh * a.group;
+    hend = head + a.group;
+    start();
+  }
+  __device__ void start() {
+    const size_t row = row0 + (size_t)head * nkb;
+    walk = TileWalker(sel_k + row * nqb, cnt_k[row], bx, sq);
+  }
+  __device__ bool next(int& hd, int& tile, uint64_t& bits) {
+    while (true) {
+      if (walk.next(tile, bits)) {
+        hd = head;
+        return true;
+      }
+      if (++head >= hend) return false;
+      start();
+    }
+  }
+};
+
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (B < E) {
@@ -150,15 +187,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   }
 
   WindowSourceDesc wsrc{};
-  BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
+  BlockGroupSource bsrc{};
   if constexpr (MASK == MASK_WINDOW) {
     const int qend = min(a.Sq, c0 + BC + a.window - 1);
     const int tlo = c0 >> 6;
     const int thi = (qend + 63) >> 6;
     wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
   } else {
-    const size_t row = kvhead * a.nkb + kblock;
-    bsrc = BlockSource{TileWalker(a.sel_k + row * a.nqb, a.cnt_k[row], a.bx, a.Sq), kvh};
+    bsrc.init(a, b, kvh, kblock);
   }
   auto fetch = [&](TileRef& r) -> bool {
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);

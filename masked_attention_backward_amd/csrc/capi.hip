@@ -203,12 +203,12 @@ size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D
 }
 
 static int block_common(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* workspace,
-                        size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
-                        int dtype) {
-  int st = check_common(B, N, N, Sq, D, scale, dtype);
+                        size_t workspace_bytes, int B, int N, int Nkv, int Sq, int Skv, int D, int bx, int by,
+                        float scale, int dtype) {
+  int st = check_common(B, N, Nkv, Sq, D, scale, dtype);
   if (st) return st;
   if (Skv < 1) return MA_EINVAL;
-  if (!sizes_fit(B, N, Skv)) return MA_EUNSUPPORTED;
+  if (!sizes_fit(B, N, Skv) || !sizes_fit(B, Nkv, Skv)) return MA_EUNSUPPORTED;
   st = check_blocks(bx, by);
   if (st) return st;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !block_mask) return MA_EINVAL;
@@ -217,10 +217,12 @@ static int block_common(const void* q, const void* k, const void* v, const uint8
   return MA_OK;
 }
 
-int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* o, float* lse,
-                         void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
-                         int by, float scale, int dtype, void* stream) {
-  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, N, Sq, Skv, D, bx, by, scale, dtype);
+int blocksparse_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* o,
+                             float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq,
+                             int Skv, int D, int bx, int by, float scale, int dtype, void* stream) {
+  const int N = Hq;
+  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, Hq, Hkv, Sq, Skv, D, bx, by, scale,
+                        dtype);
   if (st) return st;
   if (!tensor_ok(o) || !lse || !aligned(lse, 4)) return MA_EINVAL;
   const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
@@ -230,7 +232,7 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
                                         at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
                                         at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), hs);
   if (e != hipSuccess) return MA_ELAUNCH;
-  AttnArgs a = base_args(q, k, v, B, N, N, Sq, Skv, scale);
+  AttnArgs a = base_args(q, k, v, B, Hq, Hkv, Sq, Skv, scale);
   a.out_o = o;
   a.out_lse = lse;
   a.mask = block_mask;
@@ -245,11 +247,19 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
   return status_of(ma::launch_fwd(dtype, a, ma::MASK_BLOCK, hs));
 }
 
+int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
+                         int by, float scale, int dtype, void* stream) {
+  return blocksparse_attn_fwd_gqa(q, k, v, block_mask, o, lse, workspace, workspace_bytes, B, N, N, Sq, Skv, D, bx,
+                                  by, scale, dtype, stream);
+}
+
 static int block_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                           const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv,
-                          void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
-                          int by, float scale, int dtype, void* stream, void* const* events) {
-  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, N, Sq, Skv, D, bx, by, scale, dtype);
+                          void* workspace, size_t workspace_bytes, int B, int N, int Nkv, int Sq, int Skv, int D,
+                          int bx, int by, float scale, int dtype, void* stream, void* const* events) {
+  int st = block_common(q, k, v, block_mask, workspace, workspace_bytes, B, N, Nkv, Sq, Skv, D, bx, by, scale,
+                        dtype);
   if (st) return st;
   if (!tensor_ok(o) || !tensor_ok(dout) || !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv)) return MA_EINVAL;
   if (!lse || !aligned(lse, 4)) return MA_EINVAL;
@@ -266,7 +276,7 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
   e = ma::launch_preprocess(dtype, o, dout, lse, nullptr, delta, lse2, nullptr, B, N, Sq, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
   if (events) hipEventRecord((hipEvent_t)events[1], hs);
-  AttnArgs a = base_args(q, k, v, B, N, N, Sq, Skv, scale);
+  AttnArgs a = base_args(q, k, v, B, N, Nkv, Sq, Skv, scale);
   a.dout = dout;
   a.lse = lse;
   a.lse2 = lse2;
@@ -292,8 +302,16 @@ int blocksparse_attn_bwd(const void* q, const void* k, const void* v, const void
                          const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx, int by, float scale,
                          int dtype, void* stream) {
-  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, Sq, Skv, D,
-                        bx, by, scale, dtype, stream, nullptr);
+  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, N, Sq, Skv,
+                        D, bx, by, scale, dtype, stream, nullptr);
+}
+
+int blocksparse_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const uint8_t* block_mask, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D, int bx, int by,
+                             float scale, int dtype, void* stream) {
+  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Sq,
+                        Skv, D, bx, by, scale, dtype, stream, nullptr);
 }
 
 int blocksparse_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -301,8 +319,8 @@ int blocksparse_attn_bwd_timed(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, int B, int N, int Sq, int Skv, int D, int bx,
                                int by, float scale, int dtype, void* stream, void* const* events) {
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return MA_EINVAL;
-  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, Sq, Skv, D,
-                        bx, by, scale, dtype, stream, events);
+  return block_bwd_impl(q, k, v, o, dout, lse, block_mask, dq, dk, dv, workspace, workspace_bytes, B, N, N, Sq, Skv,
+                        D, bx, by, scale, dtype, stream, events);
 }
 
 }  // extern "C"

@@ -160,6 +160,8 @@ def custom_sink(name, B, Hq, Hkv, S, window, dtype=torch.float16, D=128, seed_ba
 
 
 def custom_blocksparse(name, B, N, Sq, Skv, bx, by, pattern, dtype=torch.float16, D=128, density=0.3,
-                       seed_base=200):
-    return Workload(name, BLOCKSPARSE, B, N, N, Sq, Skv, D, dtype, bx=bx, by=by, pattern=pattern,
-                    density=density, seed_base=seed_base)
+                       seed_base=200, Nkv=None):
+    """Block-sparse workload with N query heads (the mask is per query head) and Nkv K/V heads
+    (default N: MHA)."""
+    return Workload(name, BLOCKSPARSE, B, N, N if Nkv is None else Nkv, Sq, Skv, D, dtype, bx=bx, by=by,
+                    pattern=pattern, density=density, seed_base=seed_base)

@@ -107,3 +107,20 @@ def test_blocksparse_validation(lib):
     t.argtypes = [V, I, I, I, I, V, V, V, V, V, V]
     assert t(P, 1, 1, 0, 4, P, P, P, P, P, None) == EINVAL
     assert t(0, 1, 1, 4, 4, P, P, P, P, P, None) == EINVAL
+
+
+def test_blocksparse_gqa_validation(lib):
+    V, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    f = lib.blocksparse_attn_bwd_gqa
+    f.argtypes = [V] * 10 + [V, Z] + [I] * 8 + [F, I, V]
+    g = lib.blocksparse_attn_fwd_gqa
+    g.argtypes = [V] * 7 + [Z] + [I] * 8 + [F, I, V]
+
+    def call(Hq=4, Hkv=2, bx=64, ws_bytes=1 << 20):
+        return f(P, P, P, P, P, P, P, P, P, P, P, ws_bytes, 1, Hq, Hkv, 256, 256, 128, bx, 64, 0.088, F16, None)
+
+    assert call(Hkv=3) == EINVAL          # Hq % Hkv != 0
+    assert call(Hkv=0) == EINVAL
+    assert call(bx=40) == EUNSUP
+    assert call(ws_bytes=16) == EWS
+    assert g(P, P, P, P, P, P, P, 1 << 20, 1, 4, 3, 256, 256, 128, 64, 64, 0.088, F16, None) == EINVAL

@@ -120,6 +120,42 @@ def test_bwd_empty_block_shares_tile():
     check("dv", dv, ref["dv"], wl.dtype)
 
 
+GQA = [
+    W.custom_blocksparse("gqa_b64_bigbird_4to2", 1, 4, 320, 320, 64, 64, "bigbird", seed_base=301, Nkv=2),
+    W.custom_blocksparse("gqa_b48x80_random_6to2_bf16", 2, 6, 250, 230, 48, 80, "random", dtype=torch.bfloat16,
+                         density=0.4, seed_base=302, Nkv=2),
+    W.custom_blocksparse("gqa_b32x128_causal_8to1", 1, 8, 300, 300, 32, 128, "causal", seed_base=303, Nkv=1),
+]
+
+
+@pytest.mark.parametrize("wl", GQA, ids=lambda w: w.name)
+def test_bwd_gqa(wl):
+    """Grouped K/V heads: dK/dV of a K/V head sum over its query heads, each with its own mask."""
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    assert x["k"].shape[1] == wl.Hkv < wl.Hq
+    dq, dk, dv = gpu_bwd(wl, x)
+    ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
+                                                wl.bx, wl.by, wl.scale)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+@pytest.mark.parametrize("wl", GQA[:2], ids=lambda w: w.name)
+def test_fwd_gqa(wl):
+    x = W.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] blocksparse_attn_fwd (gqa) {wl.name}", flush=True)
+    o, lse = api().blocksparse_attn_fwd(g["q"], g["k"], g["v"], g["block_mask"], wl.bx, wl.by, wl.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.blocksparse_attention_forward(x["q"], x["k"], x["v"], x["block_mask"], wl.bx, wl.by, wl.scale)
+    check("o", o, ro, wl.dtype)
+    lg = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.all(np.abs(lg[fin] - rl[fin]) <= 1e-5 + 1e-5 * np.abs(rl[fin]))
+
+
 def test_ragged_config_full():
     wl = W.WORKLOADS["ragged"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
