@@ -97,6 +97,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // wait for it to complete before the next LDS read, which serialises the whole
 // prefetch.  The kernels order these copies against their LDS reads themselves: an
 // explicit vmcnt wait by every wave, then a workgroup barrier, before a stage is read.
+// M0 (the LDS destination) is set inside each statement and declared clobbered; nothing
+// else in these kernels reads M0 (on gfx950 LDS instructions do not use it), so no
+// compiler-held value lives there across the copies.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "m0");
