@@ -15,8 +15,13 @@ quoted on; every tensor is ~N(0,1) drawn in float32 and rounded to nearest-even)
   ragged        block-sparse MHA, B2 N8 Sq=Skv=3000 D128, bx=48 by=80, Bernoulli(0.3)
                 with the diagonal forced on, fp16
 
+Packed variable-length sequences (``varlen_inputs``): q, dO [Hq, total, D], k, v
+[Hkv, total, D], sink [Hq] and cu_seqlens [B + 1] int32.  The pages' varlen row gives batch
+8, 64 heads, groups 16 (read as 16 query heads per K/V head: Hkv = 4) and 2048 tokens; the
+lengths are drawn uniformly from [max/2, max] (t = 6) with the first set to max.
+
 Seeds: numpy ``default_rng(1000 * seed_base + t)`` with t = 0 for q, 1 k, 2 v, 3 dO,
-4 sink, 5 mask.  The bigbird reading: for query block i keep {i}, the global columns
+4 sink, 5 mask, 6 sequence lengths.  The bigbird reading: for query block i keep {i}, the global columns
 {0, 1} that lie at or before i, and 3 distinct columns drawn uniformly from [2, i-1]
 (all of them when fewer exist).  The ragged reading: Bernoulli(0.3) per block, then every
 key block whose token range overlaps the query block's token range is forced on, so no
@@ -165,3 +170,30 @@ def custom_blocksparse(name, B, N, Sq, Skv, bx, by, pattern, dtype=torch.float16
     (default N: MHA)."""
     return Workload(name, BLOCKSPARSE, B, N, N if Nkv is None else Nkv, Sq, Skv, D, dtype, bx=bx, by=by,
                     pattern=pattern, density=density, seed_base=seed_base)
+
+
+def varlen_lengths(B, max_len, seed_base=300):
+    """B sequence lengths, uniform on [max(1, max_len // 2), max_len], the first one max_len."""
+    rng = np.random.default_rng(1000 * seed_base + 6)
+    n = rng.integers(max(1, max_len // 2), max_len + 1, size=B)
+    n[0] = max_len
+    return [int(x) for x in n]
+
+
+def varlen_inputs(lengths, Hq, Hkv, dtype=torch.float16, D=128, seed_base=300):
+    """CPU tensors of a packed batch with the given sequence lengths (zeros allowed):
+    q, do [Hq, total, D], k, v [Hkv, total, D] in dtype, sink [Hq] fp32, cu_seqlens [B + 1]
+    int32 and max_seqlen (int)."""
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    total = int(cu[-1])
+    s = 1000 * seed_base
+    return {
+        "q": _normal(s + 0, (Hq, total, D), dtype),
+        "k": _normal(s + 1, (Hkv, total, D), dtype),
+        "v": _normal(s + 2, (Hkv, total, D), dtype),
+        "do": _normal(s + 3, (Hq, total, D), dtype),
+        "sink": _normal(s + 4, (Hq,), torch.float32),
+        "cu_seqlens": torch.from_numpy(cu.astype(np.int32)),
+        "max_seqlen": max(1, max(lengths)),
+    }

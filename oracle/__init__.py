@@ -21,6 +21,9 @@ from .attention import (  # noqa: F401
     sink_attention_forward,
     sink_attention_backward,
     sink_attention_backward_sampled,
+    packed_window_visibility,
+    sink_attention_forward_varlen,
+    sink_attention_backward_varlen,
     blocksparse_attention_forward,
     blocksparse_attention_backward,
     blocksparse_attention_backward_sampled,

@@ -236,6 +236,62 @@ def sink_attention_backward(q, k, v, o, do, lse, sink, window, scale):
     return {"dq": dq, "dk": dk, "dv": dv, "dsink": dsink, "delta": delta}
 
 
+# ------------------------------------------------- path A over packed variable-length sequences
+
+def packed_window_visibility(cu_seqlens, rows, cols, window):
+    """Packed sequences (page 1's "GQA Sink ... VarLen" rows; layout [H, total, D] is this
+    oracle's reading): row i sees row j iff both lie in one sequence b, cu[b] <= i, j <
+    cu[b+1], and 0 <= i - j < window (the window counts within the sequence)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    # Sequence index of a row; rows outside [cu[0], cu[B]) belong to no sequence (-1).
+    seg_r = np.searchsorted(cu, rows, side="right") - 1
+    seg_c = np.searchsorted(cu, cols, side="right") - 1
+    nseq = len(cu) - 1
+    seg_r = np.where((rows >= cu[0]) & (rows < cu[-1]), seg_r, -1)
+    seg_c = np.where((cols >= cu[0]) & (cols < cu[-1]), seg_c, -2)
+    return (seg_r[:, None] == seg_c[None, :]) & (seg_r[:, None] >= 0) & (seg_r[:, None] < nseq) & \
+        window_visibility(rows, cols, window)
+
+
+def sink_attention_forward_varlen(q, k, v, sink, cu_seqlens, window, scale):
+    """O [Hq,total,D] and lse [Hq,total] (fp64) over packed sequences: the sink-and-window
+    definition with visibility restricted to each sequence."""
+    q, k, v, sink = _f64(q), _f64(k), _f64(v), _f64(sink)
+    hq, total, d = q.shape
+    g = hq // k.shape[0]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    fn = lambda rows, cols: packed_window_visibility(cu, rows, cols, window)
+    o = np.zeros((hq, total, d))
+    lse = np.zeros((hq, total))
+    for h in range(hq):
+        o[h], lse[h] = _head_forward(q[h], k[h // g], v[h // g], float(sink[h]), fn, scale)
+    return o, lse
+
+
+def sink_attention_backward_varlen(q, k, v, o, do, lse, sink, cu_seqlens, window, scale):
+    """dq, dk, dv [heads, total, D], dsink [Hq] and delta [Hq, total] over packed sequences;
+    dsink sums over every row of every sequence."""
+    q, k, v, o, do, lse, sink = (_f64(x) for x in (q, k, v, o, do, lse, sink))
+    hq, total, d = q.shape
+    g = hq // k.shape[0]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    fn = lambda rows, cols: packed_window_visibility(cu, rows, cols, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.zeros((hq, total))
+    dsink = np.zeros(hq)
+    for h in range(hq):
+        kvh = h // g
+        dq[h], dk_h, dv_h, delta[h] = _head_backward(q[h], k[kvh], v[kvh], o[h], do[h], lse[h], fn, scale)
+        dk[kvh] += dk_h
+        dv[kvh] += dv_h
+        dsink[h] -= (_sink_probability(float(sink[h]), lse[h]) * delta[h]).sum()
+    return {"dq": dq, "dk": dk, "dv": dv, "dsink": dsink, "delta": delta}
+
+
 def sink_attention_backward_sampled(q, k, v, o, do, lse, sink, window, scale, q_rows, kv_rows):
     """The same definition evaluated only at chosen outputs.
 

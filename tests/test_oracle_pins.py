@@ -341,3 +341,74 @@ def test_sampled_matches_full_blocksparse():
     for t, (b, n, j) in enumerate(ks):
         assert np.allclose(sm["dk"][t], g["dk"][b, n, j], rtol=0, atol=1e-12)
         assert np.allclose(sm["dv"][t], g["dv"][b, n, j], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- packed variable-length sequences
+
+def test_packed_visibility_brute_force():
+    """Visibility over packed rows against a per-pair loop: same sequence and inside the
+    window; empty sequences and rows outside every sequence (cu[0] > 0, cu[B] < total)."""
+    cu = [2, 5, 5, 6, 11, 11]
+    total, window = 13, 3
+    rows = np.arange(total)
+    vis = oracle.packed_window_visibility(cu, rows, rows, window)
+    for i in range(total):
+        for j in range(total):
+            same = any(cu[b] <= i < cu[b + 1] and cu[b] <= j < cu[b + 1] for b in range(len(cu) - 1))
+            assert vis[i, j] == (same and 0 <= i - j < window), (i, j)
+
+
+@pytest.mark.parametrize("window", [4, 1000])
+def test_varlen_equals_per_sequence_dense(window):
+    """Every sequence of the packed definition is the dense definition on its own rows (B = 1),
+    and dsink is the sum of the per-sequence dsinks; empty and one-row sequences included."""
+    rng = np.random.default_rng(window)
+    lengths = [7, 0, 19, 1, 12]
+    Hq, Hkv, D, scale = 4, 2, 16, 0.35
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    q, do = _rand(rng, Hq, T, D), _rand(rng, Hq, T, D)
+    k, v = _rand(rng, Hkv, T, D), _rand(rng, Hkv, T, D)
+    sink = _rand(rng, Hq)
+    o, lse = oracle.sink_attention_forward_varlen(q, k, v, sink, cu, window, scale)
+    g = oracle.sink_attention_backward_varlen(q, k, v, o, do, lse, sink, cu, window, scale)
+    dsink = np.zeros(Hq)
+    for b in range(len(lengths)):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        sl = lambda x: x[None, :, s0:s1]
+        ro, rlse = oracle.sink_attention_forward(sl(q), sl(k), sl(v), sink, window, scale)
+        assert np.max(np.abs(ro[0] - o[:, s0:s1])) < 1e-12
+        assert np.max(np.abs(rlse[0] - lse[:, s0:s1])) < 1e-12
+        rg = oracle.sink_attention_backward(sl(q), sl(k), sl(v), sl(o), sl(do), sl(lse), sink, window, scale)
+        for name in ("dq", "dk", "dv", "delta"):
+            assert np.max(np.abs(rg[name][0] - g[name][:, s0:s1])) < 1e-12, (b, name)
+        dsink += rg["dsink"]
+    assert np.max(np.abs(dsink - g["dsink"])) < 1e-12
+
+
+def test_varlen_sdpa_block_diagonal():
+    """Without a sink, the packed definition is SDPA (fp64 autograd) over the whole packed
+    batch with a block-diagonal, windowed token mask, K/V repeated over each group and dK/dV
+    summed back over it."""
+    rng = np.random.default_rng(77)
+    lengths, window = [9, 14, 3], 6
+    Hq, Hkv, D, scale = 4, 1, 8, 0.5
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    q, do = _rand(rng, Hq, T, D), _rand(rng, Hq, T, D)
+    k, v = _rand(rng, Hkv, T, D), _rand(rng, Hkv, T, D)
+    sink = np.full(Hq, -np.inf)
+    o, lse = oracle.sink_attention_forward_varlen(q, k, v, sink, cu, window, scale)
+    g = oracle.sink_attention_backward_varlen(q, k, v, o, do, lse, sink, cu, window, scale)
+    seg = np.repeat(np.arange(len(lengths)), lengths)
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    m = torch.from_numpy((seg[:, None] == seg[None, :]) & (i - j >= 0) & (i - j < window))
+    kr, vr = np.repeat(k, Hq // Hkv, axis=0), np.repeat(v, Hq // Hkv, axis=0)
+    ro, rdq, rdk, rdv = _sdpa_grads(q[None], kr[None], vr[None], do[None], scale, attn_mask=m)
+    rdk = rdk[0].reshape(Hkv, Hq // Hkv, T, D).sum(axis=1)
+    rdv = rdv[0].reshape(Hkv, Hq // Hkv, T, D).sum(axis=1)
+    for a, b in zip((o, g["dq"], g["dk"], g["dv"]), (ro[0], rdq[0], rdk, rdv)):
+        assert np.max(np.abs(a - b)) < 1e-12 * max(1.0, np.max(np.abs(b)))
+    assert np.all(g["dsink"] == 0)
