@@ -189,6 +189,41 @@ int blocksparse_attn_bwd_gqa(const void* q, const void* k, const void* v,
                              int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * (A') Sink attention over packed variable-length sequences.  Page 1's kernel table lists a
+ * "GQA Sink Backward VarLen" (and forward) workload: a batch of sequences of different
+ * lengths, each attending only to itself, with the same sink and sliding-window mask as
+ * attn_sink_fwd / attn_sink_bwd.  The pages give no layout; these calls take sequences packed
+ * along the row axis of every head:
+ *   q, o, dout, dq [Hq, total, D] dtype;  k, v, dk, dv [Hkv, total, D] dtype
+ *   lse [Hq, total] fp32 (natural log, includes the sink)
+ *   cu_seqlens [B + 1] int32, DEVICE memory: sequence b is rows cu_seqlens[b] ..
+ *     cu_seqlens[b + 1] - 1 of every head; contract: cu_seqlens[0] = 0, non-decreasing,
+ *     cu_seqlens[B] = total, every length <= max_seqlen (empty sequences allowed).
+ *   window counts within a sequence (window >= max_seqlen: causal within each sequence).
+ *   dsink [Hq] fp32 (out): summed over all sequences.
+ * Workspace: attn_sink_bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, D), same layout with S =
+ * max_seqlen, per (sequence, head) (Delta row i of sequence b, head h at [b, h, i]).
+ * The offsets are device data and are not validated; the kernels clamp them to [0, total]
+ * and each length to max_seqlen, so a table that breaks the contract gives unspecified
+ * values but never an access outside the tensors.  Rows outside every sequence are not
+ * written.  Errors as attn_sink_fwd / attn_sink_bwd, plus MA_EINVAL for a null or
+ * misaligned cu_seqlens, total < 1, max_seqlen < 1 or max_seqlen > total.  With B equal
+ * lengths S and a tensor relaid [B, H, S, D] -> [H, B*S, D] the results are attn_sink_fwd's
+ * and attn_sink_bwd's.
+ * --------------------------------------------------------------------------------- */
+int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const float* sink,
+                         const int* cu_seqlens, void* o, float* lse,
+                         int B, int total, int max_seqlen, int Hq, int Hkv, int D, int window,
+                         float scale, int dtype, void* stream);
+int attn_sink_bwd_varlen(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse, const float* sink,
+                         const int* cu_seqlens,
+                         void* dq, void* dk, void* dv, float* dsink,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int total, int max_seqlen, int Hq, int Hkv, int D, int window,
+                         float scale, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Profiling variants: identical work and results to attn_sink_bwd / blocksparse_attn_bwd,
  * and additionally record caller-created HIP events (hipEvent_t, passed as void*) on
  * `stream` between the stages, so per-stage device time can be read with

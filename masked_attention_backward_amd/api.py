@@ -31,6 +31,8 @@ EXPORTS = (
     "blocksparse_attn_bwd_timed",
     "blocksparse_attn_fwd_gqa",
     "blocksparse_attn_bwd_gqa",
+    "attn_sink_fwd_varlen",
+    "attn_sink_bwd_varlen",
 )
 
 
@@ -70,6 +72,10 @@ def _load():
     lib.blocksparse_attn_fwd_gqa.restype = I
     lib.blocksparse_attn_bwd_gqa.argtypes = [P] * 10 + [P, Z] + [I] * 8 + [F, I, P]
     lib.blocksparse_attn_bwd_gqa.restype = I
+    lib.attn_sink_fwd_varlen.argtypes = [P] * 7 + [I] * 7 + [F, I, P]
+    lib.attn_sink_fwd_varlen.restype = I
+    lib.attn_sink_bwd_varlen.argtypes = [P] * 12 + [P, Z] + [I] * 7 + [F, I, P]
+    lib.attn_sink_bwd_varlen.restype = I
     return lib
 
 
@@ -162,6 +168,56 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
         sp = (S + 63) // 64 * 64
         delta = ws[: B * Hq * sp * 4].view(torch.float32).view(B, Hq, sp)[..., :S]
         return dq, dk, dv, dsink, delta
+    return dq, dk, dv, dsink
+
+
+def _varlen_shapes(q, k, cu_seqlens, max_seqlen):
+    Hq, total, D = q.shape
+    Hkv = k.shape[0]
+    dev = q.device
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens: expected a 1-D int32 tensor of B + 1 offsets")
+    _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+    return cu_seqlens.numel() - 1, Hq, Hkv, total, D, int(max_seqlen), dev
+
+
+def attn_sink_fwd_varlen(q, k, v, sink, cu_seqlens, max_seqlen, window, scale=None):
+    """Forward over packed sequences. q [Hq,total,128], k/v [Hkv,total,128], cu_seqlens [B+1] int32
+    (device), max_seqlen a host int -> (o [Hq,total,128], lse [Hq,total])."""
+    B, Hq, Hkv, total, D, smax, dev = _varlen_shapes(q, k, cu_seqlens, max_seqlen)
+    _need(q, "q", (Hq, total, D), q.dtype, dev)
+    _need(k, "k", (Hkv, total, D), q.dtype, dev)
+    _need(v, "v", (Hkv, total, D), q.dtype, dev)
+    _need(sink, "sink", (Hq,), torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, total), dtype=torch.float32, device=dev)
+    st = lib.attn_sink_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(cu_seqlens), _ptr(o), _ptr(lse), B,
+                                  total, smax, Hq, Hkv, D, int(window), scale, _dtype_code(q), _stream(dev))
+    _check("attn_sink_fwd_varlen", st)
+    return o, lse
+
+
+def attn_sink_bwd_varlen(q, k, v, o, do, lse, sink, cu_seqlens, max_seqlen, window, scale=None, workspace=None):
+    """Backward over packed sequences (layouts as attn_sink_fwd_varlen) -> (dq, dk, dv, dsink)."""
+    B, Hq, Hkv, total, D, smax, dev = _varlen_shapes(q, k, cu_seqlens, max_seqlen)
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _need(t, name, (Hq, total, D), q.dtype, dev)
+    _need(k, "k", (Hkv, total, D), q.dtype, dev)
+    _need(v, "v", (Hkv, total, D), q.dtype, dev)
+    _need(lse, "lse", (Hq, total), torch.float32, dev)
+    _need(sink, "sink", (Hq,), torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D)
+    ws = _workspace(nbytes, dev) if workspace is None else workspace
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsink = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    st = lib.attn_sink_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(sink),
+                                  _ptr(cu_seqlens), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _ptr(ws), ws.numel(),
+                                  B, total, smax, Hq, Hkv, D, int(window), scale, _dtype_code(q), _stream(dev))
+    _check("attn_sink_bwd_varlen", st)
     return dq, dk, dv, dsink
 
 

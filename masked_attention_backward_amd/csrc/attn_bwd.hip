@@ -12,30 +12,40 @@ namespace ma {
 // exp2(s - lse2) is exactly 0 there.
 // With a sink: part[b,h,blk] = sum_{i in blk} exp(sink_h - lse_i) * Delta_i, summed in a
 // fixed order (tree over the 64 rows).
+// o, dout and lse are dense [B, H, S(, D)] when `cu` is null, else packed [H, total(, D)] with
+// sequence b at rows cu[b] .. cu[b + 1] (clamped as the attention kernels clamp them); the
+// per-row buffers stay [B, H, padded S] either way.
 template <class T, bool SINK>
 __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ sink, float* __restrict__ delta,
                                                          float* __restrict__ lse2, float* __restrict__ part, int H,
-                                                         int S, int nblk) {
+                                                         int S, int nblk, const int* __restrict__ cu, int total) {
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, rsub = tid >> 4, ch = tid & 15;
   __shared__ float sd[64];
-  const size_t head = ((size_t)b * H + h) * (size_t)S;
+  size_t head = ((size_t)b * H + h) * (size_t)S;
+  int len = S;
+  if (cu) {
+    const int s0 = min(max(cu[b], 0), total);
+    const int s1 = min(max(cu[b + 1], s0), total);
+    head = (size_t)h * total + s0;
+    len = min(s1 - s0, S);
+  }
   const size_t phead = ((size_t)b * H + h) * (size_t)nblk * 64;
   if (tid < 64) {
     const int row = blk * 64 + tid;
     // Rows past the end and rows that see no key at all (lse = -inf) get +inf: exp2(s - lse2)
     // is then exactly 0 for every s, including the -inf the kernels put on masked entries.
-    const float l = (row < S) ? lse[head + row] : -INFINITY;
+    const float l = (row < len) ? lse[head + row] : -INFINITY;
     lse2[phead + row] = (l > -INFINITY) ? l * LOG2E : INFINITY;
   }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int row = blk * 64 + pass * 16 + rsub;
     float acc = 0.f;
-    if (row < S) {
+    if (row < len) {
       const u32x4 x = ld16(o + (head + row) * HD + ch * 8);
       const u32x4 y = ld16(dout + (head + row) * HD + ch * 8);
 #pragma unroll
@@ -58,7 +68,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     if (tid < 64) {
       const int row = blk * 64 + tid;
       float v = 0.f;
-      if (row < S) v = expf(sink[h] - lse[head + row]) * sd[tid];
+      if (row < len) v = expf(sink[h] - lse[head + row]) * sd[tid];
       v += __shfl_xor(v, 32);
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 8);
@@ -89,22 +99,24 @@ __global__ __launch_bounds__(64) void dsink_reduce_kernel(const float* __restric
 // ------------------------------------------------------------------------ launchers
 template <class T>
 static hipError_t launch_preprocess_t(const void* o, const void* dout, const float* lse, const float* sink,
-                                      float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st) {
+                                      float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st,
+                                      const int* cu, int total) {
   const int nblk = (S + 63) / 64;   // Delta / lse2 rows are padded to nblk * 64
   dim3 grid(nblk, H, B);
   if (sink)
     hipLaunchKernelGGL((preprocess_kernel<T, true>), grid, dim3(256), 0, st, (const uint16_t*)o,
-                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk);
+                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk, cu, total);
   else
     hipLaunchKernelGGL((preprocess_kernel<T, false>), grid, dim3(256), 0, st, (const uint16_t*)o,
-                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk);
+                       (const uint16_t*)dout, lse, sink, delta, lse2, part, H, S, nblk, cu, total);
   return hipGetLastError();
 }
 
 hipError_t launch_preprocess(int dtype, const void* o, const void* dout, const float* lse, const float* sink,
-                             float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st) {
-  return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st)
-                    : launch_preprocess_t<F16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st);
+                             float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st,
+                             const int* cu, int total) {
+  return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st, cu, total)
+                    : launch_preprocess_t<F16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st, cu, total);
 }
 
 hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, int S, hipStream_t st) {

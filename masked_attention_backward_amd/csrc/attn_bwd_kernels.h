@@ -167,16 +167,20 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
   const uint32_t kvs_lds = __builtin_amdgcn_readfirstlane(lds_addr(kvs));
   const uint32_t sld_lds = __builtin_amdgcn_readfirstlane(lds_addr(sld));
-  const size_t kvhead = (size_t)b * a.Hkv + kvh;
-  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
-  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  kv_end = min(kv_end, skv);
+  if (c0 >= kv_end) return;   // tile past the end of a shorter packed sequence (uniform)
+  const size_t kvrow0 = ks.base + (size_t)kvh * ks.head_stride;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvrow0 * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvrow0 * HD;
   const int sq_pad = (a.Sq + 63) & ~63;
 
   // K and V of rows [c0, c0 + 64 KV_TILES) into LDS (rows past the end clamped; never stored).
 #pragma unroll
   for (int t = 0; t < Sh::KV_TILES; ++t) {
-    tile_load_async<NWV>(kvs_lds + (uint32_t)(t * TILE_BYTES), Kp, c0 + 64 * t, a.Skv, wu, lane);
-    tile_load_async<NWV>(kvs_lds + (uint32_t)((Sh::KV_TILES + t) * TILE_BYTES), Vp, c0 + 64 * t, a.Skv, wu, lane);
+    tile_load_async<NWV>(kvs_lds + (uint32_t)(t * TILE_BYTES), Kp, c0 + 64 * t, skv, wu, lane);
+    tile_load_async<NWV>(kvs_lds + (uint32_t)((Sh::KV_TILES + t) * TILE_BYTES), Vp, c0 + 64 * t, skv, wu, lane);
   }
 
   f32x16 dk[4], dv[4];
@@ -189,7 +193,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   WindowSourceDesc wsrc{};
   BlockGroupSource bsrc{};
   if constexpr (MASK == MASK_WINDOW) {
-    const int qend = min(a.Sq, c0 + BC + a.window - 1);
+    const int qend = min(sq, c0 + BC + a.window - 1);
     const int tlo = c0 >> 6;
     const int thi = (qend + 63) >> 6;
     wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
@@ -203,8 +207,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   StageLoads<NWV> nx;
   auto issue = [&](const TileRef& r, int stg) {
     const size_t qhead = (size_t)b * a.Hq + r.head;
-    nx.prepare((const uint16_t*)a.q + qhead * a.Sq * HD, (const uint16_t*)a.dout + qhead * a.Sq * HD,
-               stages_lds + (uint32_t)(stg * STAGE_BYTES), r.tile * 64, a.Sq, wu, lane);
+    const size_t qrow0 = qs.base + (size_t)r.head * qs.head_stride;
+    nx.prepare((const uint16_t*)a.q + qrow0 * HD, (const uint16_t*)a.dout + qrow0 * HD,
+               stages_lds + (uint32_t)(stg * STAGE_BYTES), r.tile * 64, sq, wu, lane);
 #pragma unroll
     for (int i = 0; i < 2 * StageLoads<NWV>::J; ++i) nx.issue(i, wu);
     const uint32_t rows = sld_lds + (uint32_t)(stg * 512);
@@ -383,8 +388,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   }
   __syncthreads();
   if (qh == 0) {
-    uint16_t* dKp = (uint16_t*)a.dk + kvhead * a.Skv * HD;
-    uint16_t* dVp = (uint16_t*)a.dv + kvhead * a.Skv * HD;
+    uint16_t* dKp = (uint16_t*)a.dk + kvrow0 * HD;
+    uint16_t* dVp = (uint16_t*)a.dv + kvrow0 * HD;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
@@ -529,17 +534,22 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  q_end = min(q_end, sq);
+  if (r0 >= q_end) return;   // tile past the end of a shorter packed sequence (uniform)
   const size_t qhead = (size_t)b * a.Hq + hq;
+  const size_t qrow0 = qs.base + (size_t)hq * qs.head_stride;
   const int kvh = hq / a.group;
-  const size_t kvhead = (size_t)b * a.Hkv + kvh;
-  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
-  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const size_t kvrow0 = ks.base + (size_t)kvh * ks.head_stride;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvrow0 * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvrow0 * HD;
   const int sq_pad = (a.Sq + 63) & ~63;
 
   const int qi = r0 + 32 * w + c;
-  const int qr = min(qi, a.Sq - 1);
-  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
-  const uint16_t* Op = (const uint16_t*)a.dout + (qhead * a.Sq + qr) * HD;
+  const int qr = min(qi, sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qrow0 + qr) * HD;
+  const uint16_t* Op = (const uint16_t*)a.dout + (qrow0 + qr) * HD;
   u32x4 qf[8], of[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -556,7 +566,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   BlockSource bsrc{TileWalker(nullptr, 0, 1, 1), 0};
   if constexpr (MASK == MASK_WINDOW) {
     const int lo = max(0, r0 - a.window + 1);
-    const int hi = min(a.Skv, r0 + BQ);
+    const int hi = min(skv, r0 + BQ);
     const int tlo = lo >> 6, thi = (hi + 63) >> 6;
     wsrc = WindowSource::make(0, 1, tlo, max(0, thi - tlo));
   } else {
@@ -569,8 +579,8 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   };
   auto issue = [&](int t, int stg) {
     const uint32_t dst = stages_lds + (uint32_t)(stg * STAGE_BYTES);
-    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, wu, lane);
-    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, a.Skv, wu, lane);
+    tile_load_async<NW>(dst, Kp, t * 64, skv, wu, lane);
+    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, skv, wu, lane);
   };
 
   const float sl2 = a.scale_log2;
@@ -611,7 +621,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   while (vcur) vcur = step();
 
   // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
-  uint16_t* dQp = (uint16_t*)a.dq + qhead * a.Sq * HD;
+  uint16_t* dQp = (uint16_t*)a.dq + qrow0 * HD;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll

@@ -27,15 +27,20 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  q_end = min(q_end, sq);
+  if (r0 >= q_end) return;   // tile past the end of a shorter packed sequence (uniform)
   const size_t qhead = (size_t)b * a.Hq + hq;
+  const size_t qrow0 = qs.base + (size_t)hq * qs.head_stride;
   const int kvh = hq / a.group;
-  const size_t kvhead = (size_t)b * a.Hkv + kvh;
-  const uint16_t* Kp = (const uint16_t*)a.k + kvhead * a.Skv * HD;
-  const uint16_t* Vp = (const uint16_t*)a.v + kvhead * a.Skv * HD;
+  const size_t kvrow0 = ks.base + (size_t)kvh * ks.head_stride;
+  const uint16_t* Kp = (const uint16_t*)a.k + kvrow0 * HD;
+  const uint16_t* Vp = (const uint16_t*)a.v + kvrow0 * HD;
 
   const int qi = r0 + 32 * w + c;
-  const int qr = min(qi, a.Sq - 1);
-  const uint16_t* Qp = (const uint16_t*)a.q + (qhead * a.Sq + qr) * HD;
+  const int qr = min(qi, sq - 1);
+  const uint16_t* Qp = (const uint16_t*)a.q + (qrow0 + qr) * HD;
   u32x4 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = ld16(Qp + ks * 16 + 8 * h);
@@ -58,7 +63,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
   TileWalker walk(nullptr, 0, 1, 1);
   if constexpr (MASK == MASK_WINDOW) {
     const int lo = max(0, r0 - a.window + 1);
-    const int hi = min(a.Skv, r0 + BQ);
+    const int hi = min(skv, r0 + BQ);
     tlo = lo >> 6;
     nt = max(0, ((hi + 63) >> 6) - tlo);
   } else {
@@ -78,8 +83,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
   };
   auto issue = [&](int t, int stg) {
     const uint32_t dst = stages_lds + (uint32_t)(stg * STAGE_BYTES);
-    tile_load_async<NW>(dst, Kp, t * 64, a.Skv, wu, lane);
-    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, a.Skv, wu, lane);
+    tile_load_async<NW>(dst, Kp, t * 64, skv, wu, lane);
+    tile_load_async<NW>(dst + TILE_BYTES, Vp, t * 64, skv, wu, lane);
   };
 
   const float sl2 = a.scale_log2;
@@ -181,7 +186,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
   // Epilogue: lane (c, h) holds O^T[d = nb*32 + 8(r/4) + 4h + r%4][q = qi].
   if (qi < q_end) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    uint16_t* Orow = (uint16_t*)a.out_o + (qhead * a.Sq + qi) * HD;
+    uint16_t* Orow = (uint16_t*)a.out_o + (qrow0 + qi) * HD;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
@@ -192,7 +197,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
         st8(Orow + nb * 32 + 8 * g4 + 4 * h, v);
       }
     }
-    if (h == 0) a.out_lse[qhead * a.Sq + qi] = (l > 0.f) ? (m2 + __log2f(l)) * LN2 : -INFINITY;
+    if (h == 0) a.out_lse[qrow0 + qi] = (l > 0.f) ? (m2 + __log2f(l)) * LN2 : -INFINITY;
   }
 }
 

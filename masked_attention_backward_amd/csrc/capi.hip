@@ -129,7 +129,8 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
 static int sink_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink,
                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int window,
-                         float scale, int dtype, void* stream, void* const* events) {
+                         float scale, int dtype, void* stream, void* const* events, const int* cu = nullptr,
+                         int total = 0) {
   int st = check_common(B, Hq, Hkv, S, D, scale, dtype);
   if (st) return st;
   if (window < 1) return MA_EINVAL;
@@ -147,7 +148,7 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   float* part = at<float>(workspace, 2 * rows);
 
   if (events) hipEventRecord((hipEvent_t)events[0], hs);
-  hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, lse2, part, B, Hq, S, hs);
+  hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, lse2, part, B, Hq, S, hs, cu, total);
   if (e != hipSuccess) return MA_ELAUNCH;
   e = ma::launch_dsink_reduce(part, dsink, B, Hq, S, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
@@ -161,6 +162,8 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.cu = cu;
+  a.total = total;
   a.window = window < S ? window : S;
   e = ma::launch_window_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
   if (events) hipEventRecord((hipEvent_t)events[3], hs);
@@ -182,6 +185,45 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const void*
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return MA_EINVAL;
   return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, workspace, workspace_bytes, B, Hq, Hkv, S, D,
                        window, scale, dtype, stream, events);
+}
+
+// Packed sequences: B sequences of at most max_seqlen rows at offsets cu_seqlens[0..B] of
+// [H, total, D] tensors; scalar checks only (the offsets are device data).
+static int varlen_check(const int* cu_seqlens, int B, int total, int max_seqlen, int Hq) {
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return MA_EINVAL;
+  if (total < 1 || max_seqlen < 1 || max_seqlen > total) return MA_EINVAL;
+  if (!sizes_fit(1, Hq, total)) return MA_EUNSUPPORTED;
+  return MA_OK;
+}
+
+int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const float* sink, const int* cu_seqlens,
+                         void* o, float* lse, int B, int total, int max_seqlen, int Hq, int Hkv, int D, int window,
+                         float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, max_seqlen, D, scale, dtype);
+  if (st) return st;
+  st = varlen_check(cu_seqlens, B, total, max_seqlen, Hq);
+  if (st) return st;
+  if (window < 1) return MA_EINVAL;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return MA_EINVAL;
+  if (!sink || !aligned(sink, 4) || !lse || !aligned(lse, 4)) return MA_EINVAL;
+  AttnArgs a = base_args(q, k, v, B, Hq, Hkv, max_seqlen, max_seqlen, scale);
+  a.sink = sink;
+  a.out_o = o;
+  a.out_lse = lse;
+  a.cu = cu_seqlens;
+  a.total = total;
+  a.window = window < max_seqlen ? window : max_seqlen;
+  return status_of(ma::launch_fwd(dtype, a, ma::MASK_WINDOW, (hipStream_t)stream));
+}
+
+int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, const float* sink, const int* cu_seqlens, void* dq, void* dk, void* dv,
+                         float* dsink, void* workspace, size_t workspace_bytes, int B, int total, int max_seqlen,
+                         int Hq, int Hkv, int D, int window, float scale, int dtype, void* stream) {
+  const int st = varlen_check(cu_seqlens, B, total, max_seqlen, Hq);
+  if (st) return st;
+  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, workspace, workspace_bytes, B, Hq, Hkv,
+                       max_seqlen, D, window, scale, dtype, stream, nullptr, cu_seqlens, total);
 }
 
 int blocksparse_build_tables(const uint8_t* block_mask, int B, int N, int nqb, int nkb, uint8_t* mask_t,

@@ -160,7 +160,28 @@ struct AttnArgs {
   float scale, scale_log2;
   int n_tiles;           // stationary tiles per head (window path)
   int pair;              // 1: workgroup p also runs tile n_tiles-1-p
+  const int* cu;         // packed sequences: [B + 1] row offsets (nullptr: dense [B, H, S, D])
+  int total;             // packed sequences: rows per head of every tensor
 };
+
+// Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per
+// sequence.  Packed: [H, total, D] with sequence b at rows cu[b] .. cu[b + 1] of every head;
+// the offsets are clamped to [0, total] and the length to S (the longest sequence), so any
+// offset table keeps every access inside the tensors and the padded per-row buffers.
+// Row r of head h of the sequence is row base + h * head_stride + r.
+struct SeqRows {
+  size_t head_stride, base;
+  int len;
+};
+
+__device__ __forceinline__ SeqRows seq_rows(const AttnArgs& a, int b, int H, int S) {
+  if (a.cu) {
+    const int s0 = min(max(a.cu[b], 0), a.total);
+    const int s1 = min(max(a.cu[b + 1], s0), a.total);
+    return SeqRows{(size_t)a.total, (size_t)s0, min(s1 - s0, S)};
+  }
+  return SeqRows{(size_t)S, (size_t)b * H * S, S};
+}
 
 enum { MASK_WINDOW = 0, MASK_BLOCK = 1 };
 

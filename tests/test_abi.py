@@ -124,3 +124,28 @@ def test_blocksparse_gqa_validation(lib):
     assert call(bx=40) == EUNSUP
     assert call(ws_bytes=16) == EWS
     assert g(P, P, P, P, P, P, P, 1 << 20, 1, 4, 3, 256, 256, 128, 64, 64, 0.088, F16, None) == EINVAL
+
+
+def test_varlen_validation(lib):
+    """Scalar checks of the packed-sequence calls: each returns its status before any launch."""
+    V, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    f = lib.attn_sink_bwd_varlen
+    f.argtypes = [V] * 12 + [V, Z] + [I] * 7 + [F, I, V]
+    g = lib.attn_sink_fwd_varlen
+    g.argtypes = [V] * 7 + [I] * 7 + [F, I, V]
+
+    def call(cu=P, B=2, total=300, smax=200, Hq=4, Hkv=2, D=128, window=64, ws_bytes=1 << 24, dtype=F16):
+        return f(P, P, P, P, P, P, P, cu, P, P, P, P, P, ws_bytes, B, total, smax, Hq, Hkv, D, window, 0.088, dtype,
+                 None)
+
+    assert call(cu=None) == EINVAL
+    assert call(cu=P + 2) == EINVAL                          # misaligned offsets
+    assert call(total=0) == EINVAL
+    assert call(smax=0) == EINVAL
+    assert call(smax=301) == EINVAL                          # longer than the packed rows
+    assert call(Hkv=3) == EINVAL
+    assert call(window=0) == EINVAL
+    assert call(D=64) == EUNSUP
+    assert call(ws_bytes=16) == EWS
+    assert g(P, P, P, P, None, P, P, 2, 300, 200, 4, 2, 128, 64, 0.088, F16, None) == EINVAL
+    assert g(P, P, P, P, P, P, P, 2, 300, 200, 4, 2, 128, 0, 0.088, F16, None) == EINVAL
