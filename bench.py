@@ -167,12 +167,62 @@ def cpu_baseline(wl, x, budget_s):
     return heads, spent, cores
 
 
+def bench_varlen(args):
+    """The sink page's varlen row: 8 packed sequences of up to 2048 tokens, 64 query heads, 4 K/V
+    heads (16 per group), D=128, fp16, causal within each sequence.  One step = one
+    attn_sink_bwd_varlen call; the FLOP count sums each sequence's live tiles."""
+    import torch
+    from masked_attention_backward_amd import api, workloads as W
+
+    dev = torch.device("cuda:0")
+    lengths = W.varlen_lengths(8, 2048)
+    hq, hkv, window = 64, 4, 2048
+    x = W.varlen_inputs(lengths, hq, hkv, torch.float16)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in x.items()}
+    smax, scale = g["max_seqlen"], 1.0 / math.sqrt(128)
+    o, lse = api.attn_sink_fwd_varlen(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], smax, window, scale)
+    ws = torch.empty(api.attn_sink_bwd_workspace_bytes(len(lengths), hq, hkv, smax), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        api.attn_sink_bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], g["cu_seqlens"], smax, window,
+                                 scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = sum(live_tiles_window(L, min(window, L)) for L in lengths) * 5 * 2 * 64 * 64 * 128 * hq
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attn-bwd TFLOP/s over unmasked tiles (% fp16 MFMA peak) + bwd ms",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (seeded N(0,1) inputs, seeded lengths; O, lse from the library forward)",
+        "config": {"workload": "varlen", "B": len(lengths), "Hq": hq, "Hkv": hkv, "lengths": lengths, "D": 128,
+                   "window": window, "mask": "causal within each packed sequence + sink"},
+        "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
+        "counted_tflop": round(flops / 1e12, 4),
+        "roofline": {"kernel": "whole backward call", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_16BIT, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="large_causal")
+    ap.add_argument("--workload", default="large_causal",
+                    help="a registered workload name, or varlen (packed sequences of the sink page's varlen row)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-copy-probe", action="store_true",
@@ -186,6 +236,10 @@ def main():
               "not supported (sharding by (batch, kv-head) needs no communication and is described in the design "
               "notes, but no multi-GPU figure is produced).", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "varlen":
+        bench_varlen(args)
+        return
 
     import torch
     from masked_attention_backward_amd import api, workloads as W
