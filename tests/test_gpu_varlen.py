@@ -49,6 +49,8 @@ SMALL = [
     ("g8_w17", [129, 64, 65, 300], 8, 1, 17, torch.float16, 403),
     ("one_seq_causal_bf16", [257], 2, 2, 257, torch.bfloat16, 404),
     ("many_short", [3, 7, 1, 31, 64, 63, 65, 2, 0, 5], 2, 1, 100000, torch.float16, 405),
+    ("g4_causal_bf16", [190, 64, 0, 257, 1], 8, 2, 100000, torch.bfloat16, 408),
+    ("g6_w100", [300, 129, 40], 6, 1, 100, torch.float16, 409),
 ]
 
 
