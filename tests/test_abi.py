@@ -149,3 +149,19 @@ def test_varlen_validation(lib):
     assert call(ws_bytes=16) == EWS
     assert g(P, P, P, P, None, P, P, 2, 300, 200, 4, 2, 128, 64, 0.088, F16, None) == EINVAL
     assert g(P, P, P, P, P, P, P, 2, 300, 200, 4, 2, 128, 0, 0.088, F16, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """Without libmaskattn.so the binding refuses to import: there is no CPU or PyTorch path."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "masked_attention_backward_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "masked_attention_backward_amd", "api.py"), pkg / "api.py")
+    (pkg / "__init__.py").write_text("")
+    r = subprocess.run([sys.executable, "-c", "import masked_attention_backward_amd.api"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "no fallback" in r.stderr
