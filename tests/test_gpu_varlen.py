@@ -175,3 +175,25 @@ def test_pages_varlen_workload_sampled():
             check(f"dk[seq {b}]", torch.stack([dk[h, s0 + j] for _, h, j in ks]), ref["dk"], dtype)
             check(f"dv[seq {b}]", torch.stack([dv[h, s0 + j] for _, h, j in ks]), ref["dv"], dtype)
     check("dsink", dsink, dsink_ref, dtype)
+
+
+@pytest.mark.slow
+def test_pages_varlen_forward_two_sequences():
+    """The sink page's varlen forward row at full size (8 sequences of up to 2048 tokens, 64 query
+    heads, 4 K/V heads, fp16, causal within each sequence): every O and lse row of two of the
+    sequences against the dense oracle on that sequence's rows."""
+    lengths = W.varlen_lengths(8, 2048)
+    hq, hkv, dtype, window = 64, 4, torch.float16, 2048
+    x = W.varlen_inputs(lengths, hq, hkv, dtype, seed_base=310)
+    g = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
+    print("[gpu] attn_sink_fwd_varlen pages workload", flush=True)
+    o, lse = api().attn_sink_fwd_varlen(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], g["max_seqlen"], window,
+                                        SCALE)
+    torch.cuda.synchronize()
+    cu = x["cu_seqlens"].numpy().astype(np.int64)
+    for b in (0, 6):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        ro, rl = oracle.sink_attention_forward(x["q"][None, :, s0:s1], x["k"][None, :, s0:s1], x["v"][None, :, s0:s1],
+                                               x["sink"], window, SCALE)
+        check(f"o[seq {b}]", o[:, s0:s1], ro[0], dtype)
+        check(f"lse[seq {b}]", lse[:, s0:s1], rl[0], dtype)
