@@ -49,10 +49,10 @@ class Workload:
     Skv: int
     D: int
     dtype: torch.dtype
-    window: int = 0        # sink path only
+    window: int = 0        # sink path; block path: band width (tokens) of the "window" pattern
     bx: int = 0            # block-sparse only
     by: int = 0
-    pattern: str = ""      # "bigbird" | "ragged" | "random" | "dense" | "causal"
+    pattern: str = ""      # "bigbird" | "ragged" | "random" | "dense" | "causal" | "window"
     density: float = 0.3
     seed_base: int = 0
 
@@ -139,6 +139,13 @@ def make_block_mask(wl, seed=None):
                 qi = np.arange(wl.nqb)[:, None] * wl.bx
                 kj = np.arange(wl.nkb)[None, :] * wl.by
                 out[b, n] = (kj <= qi + wl.bx - 1).astype(np.uint8)
+            elif wl.pattern == "window":
+                # Blocks that meet the causal band 0 <= i - j < window of some row of the block.
+                q0 = np.arange(wl.nqb)[:, None] * wl.bx
+                q1 = np.minimum(q0 + wl.bx, wl.Sq) - 1
+                k0 = np.arange(wl.nkb)[None, :] * wl.by
+                k1 = np.minimum(k0 + wl.by, wl.Skv) - 1
+                out[b, n] = ((k0 <= q1) & (k1 >= q0 - wl.window + 1)).astype(np.uint8)
             else:
                 raise ValueError(f"unknown mask pattern {wl.pattern!r}")
     return torch.from_numpy(out)
@@ -165,11 +172,11 @@ def custom_sink(name, B, Hq, Hkv, S, window, dtype=torch.float16, D=128, seed_ba
 
 
 def custom_blocksparse(name, B, N, Sq, Skv, bx, by, pattern, dtype=torch.float16, D=128, density=0.3,
-                       seed_base=200, Nkv=None):
+                       seed_base=200, Nkv=None, window=0):
     """Block-sparse workload with N query heads (the mask is per query head) and Nkv K/V heads
-    (default N: MHA)."""
+    (default N: MHA); `window` is the band width of the "window" pattern."""
     return Workload(name, BLOCKSPARSE, B, N, N if Nkv is None else Nkv, Sq, Skv, D, dtype, bx=bx, by=by,
-                    pattern=pattern, density=density, seed_base=seed_base)
+                    pattern=pattern, density=density, seed_base=seed_base, window=window)
 
 
 def varlen_lengths(B, max_len, seed_base=300):

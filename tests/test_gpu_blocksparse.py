@@ -74,6 +74,9 @@ SMALL = [
                          seed_base=208),
     W.custom_blocksparse("b96x64_random_bf16", 1, 3, 260, 200, 96, 64, "random", dtype=torch.bfloat16,
                          density=0.5, seed_base=209),
+    W.custom_blocksparse("b64_window200_bf16", 1, 2, 450, 450, 64, 64, "window", dtype=torch.bfloat16,
+                         seed_base=210, window=200),
+    W.custom_blocksparse("b32x16_window100", 2, 1, 333, 333, 32, 16, "window", seed_base=211, window=100),
 ]
 
 
