@@ -96,6 +96,30 @@ __global__ __launch_bounds__(64) void dsink_reduce_kernel(const float* __restric
   if (lane == 0) dsink[h] = -acc;
 }
 
+// Block path, key blocks whose selected query blocks span several dK/dV workgroups: sum the
+// fp32 partials in chunk order (fixed, so results are bit-identical run to run) and cast.
+// A 256-thread block covers 8 key rows x 128 columns (4 columns per thread) of one kv head.
+template <class T>
+__global__ __launch_bounds__(256) void dkv_chunk_reduce_kernel(const AttnArgs a) {
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5), col = (threadIdx.x & 31) * 4;
+  if (row >= a.Skv) return;
+  const int nch = block_chunks(a, b, kvh, row / a.by);
+  if (nch <= 1) return;   // stored directly by its only workgroup
+  const int skv_pad = (a.Skv + 63) & ~63;
+  const size_t slot = (size_t)skv_pad * HD;
+  const size_t slab = (size_t)a.B * a.Hkv * a.max_chunks * slot;
+  const float* pk = a.dkv_part + ((size_t)b * a.Hkv + kvh) * a.max_chunks * slot + (size_t)row * HD + col;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c) {
+    sk += *reinterpret_cast<const f32x4*>(pk + c * slot);
+    sv += *reinterpret_cast<const f32x4*>(pk + slab + c * slot);
+  }
+  const size_t o = (((size_t)b * a.Hkv + kvh) * a.Skv + row) * HD + col;
+  st8((uint16_t*)a.dk + o, (u32x2){T::pack2(sk[0], sk[1]), T::pack2(sk[2], sk[3])});
+  st8((uint16_t*)a.dv + o, (u32x2){T::pack2(sv[0], sv[1]), T::pack2(sv[2], sv[3])});
+}
+
 // ------------------------------------------------------------------------ launchers
 template <class T>
 static hipError_t launch_preprocess_t(const void* o, const void* dout, const float* lse, const float* sink,
@@ -152,13 +176,15 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
 template <class T>
 static void launch_block_t(const AttnArgs& a, hipStream_t st, hipEvent_t ev_mid) {
   const int nwk = (a.by + 31) / 32, nwq = (a.bx + 31) / 32;
-  const int gk = a.B * a.Hkv * a.nkb, gq = a.B * a.Hq * a.nqb;
+  const int gk = a.B * a.Hkv * a.nkb * a.max_chunks, gq = a.B * a.Hq * a.nqb;
   switch (nwk) {
     case 1: launch_dkdv_variant<T, MASK_BLOCK, 1>(a, gk, st); break;
     case 2: launch_dkdv_variant<T, MASK_BLOCK, 2>(a, gk, st); break;
     case 3: launch_dkdv_variant<T, MASK_BLOCK, 3>(a, gk, st); break;
     default: launch_dkdv_variant<T, MASK_BLOCK, 4>(a, gk, st); break;
   }
+  if (a.max_chunks > 1)
+    hipLaunchKernelGGL(dkv_chunk_reduce_kernel<T>, dim3((a.Skv + 7) / 8, a.Hkv, a.B), dim3(256), 0, st, a);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   switch (nwq) {
     case 1: launch_dq_variant<T, MASK_BLOCK, 1>(a, gq, st); break;

@@ -83,14 +83,16 @@ struct BlockSource {
 
 // The query tiles a key block of a K/V head sees on the block path: the rows of the kv-major
 // table of every query head of its group, one head after the other (a single head for MHA).
+// A workgroup may take only a chunk of that concatenated list: entries [first, first + count).
 struct BlockGroupSource {
   const int* sel_k = nullptr;   // [B, Hq, nkb, nqb]
   const int* cnt_k = nullptr;   // [B, Hq, nkb]
   size_t row0 = 0;              // (b * Hq) * nkb + kblock: table row of query head 0
   int nkb = 0, nqb = 0, bx = 1, sq = 1;
   int head = 0, hend = 0;
+  int skip = 0, left = 0;       // entries still to skip / still to walk
   TileWalker walk{nullptr, 0, 1, 1};
-  __device__ void init(const AttnArgs& a, int b, int kvh, int kblock) {
+  __device__ void init(const AttnArgs& a, int b, int kvh, int kblock, int first, int count) {
     sel_k = a.sel_k;
     cnt_k = a.cnt_k;
     row0 = (size_t)b * a.Hq * a.nkb + kblock;
@@ -100,11 +102,18 @@ struct BlockGroupSource {
     sq = a.Sq;
     head = kvh * a.group;
     hend = head + a.group;
+    skip = first;
+    left = count;
     start();
   }
   __device__ void start() {
     const size_t row = row0 + (size_t)head * nkb;
-    walk = TileWalker(sel_k + row * nqb, cnt_k[row], bx, sq);
+    const int n = cnt_k[row];
+    const int s0 = min(skip, n);
+    const int take = min(n - s0, left);
+    skip -= s0;
+    left -= take;
+    walk = TileWalker(sel_k + row * nqb + s0, take, bx, sq);
   }
   __device__ bool next(int& hd, int& tile, uint64_t& bits) {
     while (true) {
@@ -112,11 +121,20 @@ struct BlockGroupSource {
         hd = head;
         return true;
       }
-      if (++head >= hend) return false;
+      if (++head >= hend || left <= 0) return false;
       start();
     }
   }
 };
+
+// Number of chunks the key block's concatenated table rows split into (1 when unchunked).
+__device__ __forceinline__ int block_chunks(const AttnArgs& a, int b, int kvh, int kblock) {
+  if (a.chunk <= 0) return 1;
+  const size_t row0 = ((size_t)b * a.Hq + (size_t)kvh * a.group) * a.nkb + kblock;
+  int e = 0;
+  for (int h = 0; h < a.group; ++h) e += a.cnt_k[row0 + (size_t)h * a.nkb];
+  return max(1, (e + a.chunk - 1) / a.chunk);
+}
 
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -154,7 +172,7 @@ struct DkdvShape {
 
 template <class T, int MASK, int NK>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kblock,
-                                          uint16_t* smem) {
+                                          uint16_t* smem, int chunk = 0, bool partial = false) {
   using Sh = DkdvShape<NK>;
   constexpr int NWV = Sh::NWAVES;
   constexpr int BC = 32 * NK;
@@ -198,7 +216,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     const int thi = (qend + 63) >> 6;
     wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
   } else {
-    bsrc.init(a, b, kvh, kblock);
+    if (a.chunk > 0) bsrc.init(a, b, kvh, kblock, chunk * a.chunk, a.chunk);
+    else bsrc.init(a, b, kvh, kblock, 0, 0x7fffffff);
   }
   auto fetch = [&](TileRef& r) -> bool {
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);
@@ -387,7 +406,31 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     }
   }
   __syncthreads();
-  if (qh == 0) {
+  if (qh == 0 && partial) {
+    // One chunk of a key block whose selected query blocks span several workgroups: fp32
+    // partial sums, added in chunk order and cast by the dK/dV reduce kernel.
+    const int skv_pad = (a.Skv + 63) & ~63;
+    const size_t slab = (size_t)a.B * a.Hkv * a.max_chunks * skv_pad * HD;
+    float* pk = a.dkv_part + (((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk) * skv_pad * HD;
+    float* pv = pk + slab;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 pk4 = red[(nb * 4 + q4) * 64];
+        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const int row = c0 + 32 * kb + 8 * q4 + 4 * h + e;
+          if (row < kv_end) {
+            pk[(size_t)row * HD + nb * 32 + c] = (dk[nb][r] + pk4[e]) * a.scale;
+            pv[(size_t)row * HD + nb * 32 + c] = dv[nb][r] + pv4[e];
+          }
+        }
+      }
+    }
+  } else if (qh == 0) {
     uint16_t* dKp = (uint16_t*)a.dk + kvrow0 * HD;
     uint16_t* dVp = (uint16_t*)a.dv + kvrow0 * HD;
 #pragma unroll
@@ -429,8 +472,13 @@ __global__ __launch_bounds__(2 * NK * 64) void dkdv_kernel(const AttnArgs a) {
       dkdv_tile<T, MASK, NK>(a, b, kvh, p2 * BC, a.Skv, 0, smem);
     }
   } else {
-    const int c0 = p * a.by;
-    dkdv_tile<T, MASK, NK>(a, b, kvh, c0, min(c0 + a.by, a.Skv), p, smem);
+    // p = (max_chunks - 1 - chunk) * nkb + key block: the last chunks, which only the most
+    // selected key blocks have, are dispatched first, so those blocks do not finish last.
+    const int kblock = p % a.nkb, chunk = a.max_chunks - 1 - p / a.nkb;
+    const int nch = block_chunks(a, b, kvh, kblock);
+    if (chunk >= nch) return;   // uniform: no loads or barriers issued yet
+    const int c0 = kblock * a.by;
+    dkdv_tile<T, MASK, NK>(a, b, kvh, c0, min(c0 + a.by, a.Skv), kblock, smem, chunk, nch > 1);
   }
 }
 

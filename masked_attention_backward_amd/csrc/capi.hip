@@ -47,11 +47,25 @@ int check_blocks(int bx, int by) {
   return MA_OK;
 }
 
+// Block path: a dK/dV workgroup walks at most this many selected query blocks (summed over the
+// query heads of its group); key blocks selected more often are split over several
+// workgroups whose fp32 partial sums a reduce kernel adds in a fixed order.
+constexpr int kBlockChunk = 32;
+
+// Chunks per (kv head, key block) the dK/dV grid provides: ceil(group * nqb / kBlockChunk).
+int block_max_chunks(int N, int Nkv, int nqb) {
+  const long long g = N / Nkv;
+  return (int)((g * nqb + kBlockChunk - 1) / kBlockChunk);
+}
+
 struct BlockLayout {
-  size_t delta, lse2, mask_t, sel_q, cnt_q, sel_k, cnt_k, total;
+  size_t delta, lse2, mask_t, sel_q, cnt_q, sel_k, cnt_k, part, total;
 };
 
-BlockLayout block_layout(int B, int N, int Sq, int nqb, int nkb) {
+// The partial-sum region is sized for any Nkv dividing N: Nkv * ceil((N / Nkv) * nqb / C) <=
+// floor(N * (nqb + C - 1) / C) chunk slots per batch, each of padded Skv rows of D fp32 values,
+// for dK and for dV.  It is absent when no key block can need more than one chunk.
+BlockLayout block_layout(int B, int N, int Sq, int Skv, int nqb, int nkb) {
   BlockLayout l;
   const size_t bn = (size_t)B * N;
   l.delta = 0;
@@ -61,7 +75,12 @@ BlockLayout block_layout(int B, int N, int Sq, int nqb, int nkb) {
   l.cnt_q = align256(l.sel_q + bn * nqb * nkb * sizeof(int32_t));
   l.sel_k = align256(l.cnt_q + bn * nqb * sizeof(int32_t));
   l.cnt_k = align256(l.sel_k + bn * nkb * nqb * sizeof(int32_t));
-  l.total = align256(l.cnt_k + bn * nkb * sizeof(int32_t));
+  l.part = align256(l.cnt_k + bn * nkb * sizeof(int32_t));
+  l.total = l.part;
+  if ((long long)N * nqb > kBlockChunk) {
+    const size_t slots = (size_t)B * (((size_t)N * (nqb + kBlockChunk - 1)) / kBlockChunk);
+    l.total = align256(l.part + 2 * slots * pad64(Skv) * ma::HD * sizeof(float));
+  }
   return l;
 }
 
@@ -77,6 +96,7 @@ AttnArgs base_args(const void* q, const void* k, const void* v, int B, int Hq, i
   a.Sq = Sq;
   a.Skv = Skv;
   a.group = Hq / Hkv;
+  a.max_chunks = 1;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return a;
@@ -241,7 +261,7 @@ size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D
   if (check_common(B, N, N, Sq, D, 1.f, MA_F16) != MA_OK || Skv < 1 || check_blocks(bx, by) != MA_OK) return 0;
   if (!sizes_fit(B, N, Skv)) return 0;
   const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
-  return block_layout(B, N, Sq, nqb, nkb).total;
+  return block_layout(B, N, Sq, Skv, nqb, nkb).total;
 }
 
 static int block_common(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* workspace,
@@ -256,6 +276,8 @@ static int block_common(const void* q, const void* k, const void* v, const uint8
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !block_mask) return MA_EINVAL;
   if (!workspace || !aligned(workspace, 256)) return MA_EINVAL;
   if (workspace_bytes < blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, D, bx, by)) return MA_EWORKSPACE;
+  const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
+  if ((long long)B * Nkv * nkb * block_max_chunks(N, Nkv, nqb) > 0x7fffffffll) return MA_EUNSUPPORTED;
   return MA_OK;
 }
 
@@ -268,7 +290,7 @@ int blocksparse_attn_fwd_gqa(const void* q, const void* k, const void* v, const 
   if (st) return st;
   if (!tensor_ok(o) || !lse || !aligned(lse, 4)) return MA_EINVAL;
   const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
-  const BlockLayout L = block_layout(B, N, Sq, nqb, nkb);
+  const BlockLayout L = block_layout(B, N, Sq, Skv, nqb, nkb);
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = ma::launch_mask_tables(block_mask, B * N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
                                         at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
@@ -306,7 +328,7 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
   if (!tensor_ok(o) || !tensor_ok(dout) || !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv)) return MA_EINVAL;
   if (!lse || !aligned(lse, 4)) return MA_EINVAL;
   const int nqb = (Sq + bx - 1) / bx, nkb = (Skv + by - 1) / by;
-  const BlockLayout L = block_layout(B, N, Sq, nqb, nkb);
+  const BlockLayout L = block_layout(B, N, Sq, Skv, nqb, nkb);
   hipStream_t hs = (hipStream_t)stream;
   if (events) hipEventRecord((hipEvent_t)events[0], hs);
   hipError_t e = ma::launch_mask_tables(block_mask, B * N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
@@ -335,6 +357,13 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
   a.by = by;
   a.nqb = nqb;
   a.nkb = nkb;
+  a.max_chunks = block_max_chunks(N, Nkv, nqb);
+  if (a.max_chunks > 1) {
+    a.chunk = kBlockChunk;
+    a.dkv_part = at<float>(workspace, L.part);
+  } else {
+    a.max_chunks = 1;
+  }
   e = ma::launch_block_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
   if (events) hipEventRecord((hipEvent_t)events[3], hs);
   return status_of(e);

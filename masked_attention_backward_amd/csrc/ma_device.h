@@ -162,6 +162,10 @@ struct AttnArgs {
   int pair;              // 1: workgroup p also runs tile n_tiles-1-p
   const int* cu;         // packed sequences: [B + 1] row offsets (nullptr: dense [B, H, S, D])
   int total;             // packed sequences: rows per head of every tensor
+  int chunk;             // block path: selected query blocks per dK/dV workgroup (0: no limit)
+  int max_chunks;        // block path: chunks per (kv head, key block) the grid provides for
+  float* dkv_part;       // block path, chunked key blocks: fp32 partial dK (scaled) and dV,
+                         // [2][B][Hkv][max_chunks][padded Skv][D]
 };
 
 // Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per

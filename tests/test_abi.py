@@ -84,6 +84,11 @@ def test_workspace_queries(lib):
     m = lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 80)
     nqb, nkb = 63, 38
     assert m >= 2 * 8 * (3000 * 4 + nqb * nkb * 9 + (nqb + nkb) * 4)
+    # Partial-sum region for chunked key blocks (63 query blocks > 32 per chunk): 2 x slots x
+    # padded Skv x 128 fp32, slots = B * floor(N * (nqb + 31) / 32).
+    assert m >= 2 * (2 * ((8 * (nqb + 31)) // 32)) * 3008 * 128 * 4
+    small = lib.blocksparse_attn_bwd_workspace_bytes(1, 1, 512, 512, 128, 64, 64)          # 8 query blocks
+    assert small < 4 * 512 * 4 + 2 * 1024 * 4 + 8192
     assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 40, 80) == 0    # bx % 16 != 0
     assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 144) == 0   # by > 128
 

@@ -77,6 +77,13 @@ SMALL = [
     W.custom_blocksparse("b64_window200_bf16", 1, 2, 450, 450, 64, 64, "window", dtype=torch.bfloat16,
                          seed_base=210, window=200),
     W.custom_blocksparse("b32x16_window100", 2, 1, 333, 333, 32, 16, "window", seed_base=211, window=100),
+    # Key blocks selected by more than 32 query blocks are split over several dK/dV workgroups
+    # (fp32 partials summed in chunk order): two and three chunks, and bigbird's global columns
+    # (two chunks) next to single-chunk key blocks.
+    W.custom_blocksparse("b16x32_dense_2chunks", 1, 2, 700, 300, 16, 32, "dense", seed_base=212),
+    W.custom_blocksparse("b16x64_dense_3chunks_bf16", 1, 1, 1100, 200, 16, 64, "dense", dtype=torch.bfloat16,
+                         seed_base=213),
+    W.custom_blocksparse("b64_bigbird_chunked", 1, 1, 2300, 2300, 64, 64, "bigbird", seed_base=214),
 ]
 
 
@@ -128,6 +135,8 @@ GQA = [
     W.custom_blocksparse("gqa_b48x80_random_6to2_bf16", 2, 6, 250, 230, 48, 80, "random", dtype=torch.bfloat16,
                          density=0.4, seed_base=302, Nkv=2),
     W.custom_blocksparse("gqa_b32x128_causal_8to1", 1, 8, 300, 300, 32, 128, "causal", seed_base=303, Nkv=1),
+    # The group's 4 query heads select key block 0 52 times (two chunks), the last one 4 times.
+    W.custom_blocksparse("gqa_b32_causal_chunked_4to1", 1, 4, 400, 400, 32, 32, "causal", seed_base=304, Nkv=1),
 ]
 
 
