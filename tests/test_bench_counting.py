@@ -1,9 +1,13 @@
 """The benchmark's FLOP count: live 64x64 tiles of the sliding-window causal mask (five GEMMs
 of 2*64*64*128 FLOP each per live tile), checked against closed forms and brute force."""
 
+import os
+
 import numpy as np
 
 import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def brute_live_tiles(S, W, grid=64):
@@ -33,3 +37,14 @@ def test_headline_counted_flops():
     assert per_head == 8256 * 5 * 2 * 64 * 64 * 128
     assert total == 528384 * 5 * 2 * 64 * 64 * 128
     assert abs(total - 2.7703e12) / 2.7703e12 < 1e-4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library is measured on one GPU: `bench.py --gpus 2` exits with status 2 and says so,
+    before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
