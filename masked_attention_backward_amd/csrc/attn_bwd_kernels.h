@@ -464,9 +464,12 @@ __global__ __launch_bounds__(2 * NK * 64) void dkdv_kernel(const AttnArgs a) {
     constexpr int BC = 32 * NK;
     // Workgroups of one (batch, kv head) are consecutive modulo B*Hkv: with B*Hkv = 8 they
     // all land on one XCD and share its L2.  Tile p is paired with tile n - 1 - p (equal
-    // total work) when the launcher sets `pair`.
+    // total work) when the launcher sets `pair`; n counts the tiles of this sequence, so a
+    // shorter packed sequence pairs within itself (workgroups past its middle have no work).
+    const int nk = a.cu ? (seq_rows(a, b, a.Hkv, a.Skv).len + BC - 1) / BC : a.n_tiles;
+    const int p2 = nk - 1 - p;
+    if (a.pair && p > p2) return;
     dkdv_tile<T, MASK, NK>(a, b, kvh, p * BC, a.Skv, 0, smem);
-    const int p2 = a.n_tiles - 1 - p;
     if (a.pair && p2 != p) {
       __syncthreads();
       dkdv_tile<T, MASK, NK>(a, b, kvh, p2 * BC, a.Skv, 0, smem);
@@ -688,7 +691,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
     constexpr int BQ = 32 * NW;
     int b, hq, p;
     window_q_item(a, wg, b, hq, p);
-    const int t1 = a.n_tiles - 1 - p;
+    // Heaviest query tiles first; with `pair`, tile n - 1 - p also runs tile p, n counting
+    // the tiles of this sequence.
+    const int nq = a.cu ? (seq_rows(a, b, a.Hq, a.Sq).len + BQ - 1) / BQ : a.n_tiles;
+    const int t1 = nq - 1 - p;
+    if (t1 < 0 || (a.pair && p > t1)) return;
     dq_tile<T, MASK, NW>(a, b, hq, t1 * BQ, a.Sq, 0, stages);
     const int t2 = p;
     if (a.pair && t2 != t1) {
