@@ -114,8 +114,23 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
-def _workspace(nbytes, device):
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+def _workspace(nbytes, device, given=None):
+    """The caller's workspace after checking it (uint8, contiguous, on `device`, at least
+    `nbytes` bytes), or a new one of that size."""
+    nbytes = int(nbytes)
+    if given is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if not torch.is_tensor(given):
+        raise TypeError("workspace: expected a torch.uint8 tensor")
+    if given.dtype != torch.uint8:
+        raise TypeError(f"workspace: expected torch.uint8, got {given.dtype}")
+    if given.device != device:
+        raise ValueError(f"workspace: expected device {device}, got {given.device}")
+    if not given.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    if given.numel() < nbytes:
+        raise ValueError(f"workspace: {given.numel()} bytes, at least {nbytes} needed")
+    return given
 
 
 # --------------------------------------------------------------------------- sink path
@@ -154,8 +169,7 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
     _need(lse, "lse", (B, Hq, S), torch.float32, dev)
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    nbytes = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D)
-    ws = _workspace(nbytes, dev) if workspace is None else workspace
+    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D), dev, workspace)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -208,8 +222,7 @@ def attn_sink_bwd_varlen(q, k, v, o, do, lse, sink, cu_seqlens, max_seqlen, wind
     _need(lse, "lse", (Hq, total), torch.float32, dev)
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    nbytes = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D)
-    ws = _workspace(nbytes, dev) if workspace is None else workspace
+    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D), dev, workspace)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -262,8 +275,7 @@ def blocksparse_attn_fwd(q, k, v, block_mask, bx, by, scale=None, workspace=None
     _need(k, "k", (B, Nkv, Skv, D), q.dtype, dev)
     _need(v, "v", (B, Nkv, Skv, D), q.dtype, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev) if workspace is None \
-        else workspace
+    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev, workspace)
     o = torch.empty_like(q)
     lse = torch.empty((B, N, Sq), dtype=torch.float32, device=dev)
     if Nkv == N:
@@ -287,8 +299,7 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     _need(v, "v", (B, Nkv, Skv, D), q.dtype, dev)
     _need(lse, "lse", (B, N, Sq), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev) if workspace is None \
-        else workspace
+    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev, workspace)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

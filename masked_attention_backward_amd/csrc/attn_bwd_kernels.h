@@ -342,20 +342,37 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       }
     }
     MA_STEP();
-    // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
-    // done one per MFMA between those eight MFMAs.
-    u32x4 pa[2], da[2];
-    float pk = 0.f, dk2 = 0.f;
-    f32x4 L[4];
+    // log2 P = S scale log2e - lse log2e, in place.
+    {
+      f32x4 L[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
+      for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], sl2, -L[r / 4][r % 4]);
+    }
     // First dV/dK operands, read before the softmax rows that precede their MFMAs.
     u32x4 fb[2], fc[2];
     fb[0] = frag_col(stages, fo, 1, 0, 0);
     fc[0] = frag_col(stages, fo, 0, 0, 0);
+    // P and dS enter the dV and dK products rounded to 16 bits.  Where some P of this wave's
+    // 32 x 32 block exceeds 1/4, the rounding error of such large terms, summed over every
+    // query row and head that attends strongly to one key, can approach the tolerance; those
+    // blocks (rare: the first query rows of a sequence, sharply peaked rows) also add the
+    // rounding residuals in a second product at the end of the tile (the page's compensated
+    // hi + lo GEMM), which makes their P and dS exact to about 22 bits.  The test is a
+    // ballot, uniform over the wave, so results stay deterministic.
+    float lmax = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, s[r]);
+    const bool comp = __builtin_amdgcn_ballot_w64(lmax > -2.0f) != 0;
+    MA_STEP();
+    // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
+    // done one per MFMA between those eight MFMAs.
+    u32x4 pa[2], da[2];
+    float pk = 0.f, dk2 = 0.f;
     auto srow = [&](auto rc) {
-      constexpr int r = decltype(rc)::value, g = r / 4, e = r % 4;
-      const float v = fast_exp2(fmaf(s[r], sl2, -L[g][e]));
+      constexpr int r = decltype(rc)::value;
+      const float v = fast_exp2(s[r]);
       const float dsv = -(v * d[r]);
       if constexpr ((r & 1) == 0) {
         pk = v;
@@ -381,6 +398,60 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       if constexpr (j < 4) srow(std::integral_constant<int, 9 + 2 * j>{});
       MA_STEP();
     });
+    if (comp) {
+      // Residual products of this tile: S and dP again from the stage (still resident), the
+      // same mask and exponent, then dV += (P - hi(P))^T dO and dK += (dS - hi(dS))^T Q.
+      f32x16 s2 = zero16(), d2;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d2[4 * g + e] = D4[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s2 = T::mma(frag_row(stages, fo, 0, ks, 0), frag_row(kvs, fkv, 0, ks, 0), s2);
+        d2 = T::mma(frag_row(stages, fo, 1, ks, 0), frag_row(kvs, fkv, Sh::KV_TILES, ks, 0), d2);
+      }
+      if (masked) {
+        if constexpr (MASK == MASK_WINDOW) {
+          const int qdiff = cur.tile * 64 + qh * 32 + 4 * h - kj;
+          static_for<0, 16>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            constexpr int qo = 8 * (r / 4) + (r % 4);
+            s2[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s2[r] : -INFINITY;
+          });
+        } else {
+          const uint64_t hb = cur.bits >> (qh * 32 + 4 * h);
+          static_for<0, 16>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            constexpr int qo = 8 * (r / 4) + (r % 4);
+            s2[r] = ((hb >> qo) & 1ull) ? s2[r] : -INFINITY;
+          });
+        }
+      }
+      u32x4 pl[2], dl[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L4 = *(lds_f32x4)(ld + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int r = 4 * g + e;
+          const float v0 = fast_exp2(fmaf(s2[r], sl2, -L4[e]));
+          const float v1 = fast_exp2(fmaf(s2[r + 1], sl2, -L4[e + 1]));
+          const float d0 = -(v0 * d2[r]), d1 = -(v1 * d2[r + 1]);
+          const uint32_t ph = T::pack2(v0, v1), dh = T::pack2(d0, d1);
+          pl[r / 8][(r % 8) / 2] = T::pack2(v0 - T::lo(ph), v1 - T::hi(ph));
+          dl[r / 8][(r % 8) / 2] = T::pack2(d0 - T::lo(dh), d1 - T::hi(dh));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = j / 4, nb = j % 4;
+        dv[nb] = T::mma(pl[t], frag_col(stages, fo, 1, t, nb), dv[nb]);
+        dk[nb] = T::mma(dl[t], frag_col(stages, fo, 0, t, nb), dk[nb]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       fo.row[i] ^= STAGE_BYTES;

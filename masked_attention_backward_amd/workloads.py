@@ -11,14 +11,18 @@ quoted on; every tensor is ~N(0,1) drawn in float32 and rounded to nearest-even)
   mid           GQA sink, B2 Hq32 Hkv8 S2048 D128, window 128, fp16
   large_w128    GQA sink, B1 Hq64 Hkv8 S8192 D128, window 128, bf16
   large_causal  GQA sink, B1 Hq64 Hkv8 S8192 D128, window = S (full causal), bf16
+  pages_h64_s4096  GQA sink, B1 Hq64 Hkv8 S4096 D128, window = S, fp16 (the sink page's
+                table shape)
   bigbird       block-sparse MHA, B1 N16 S8192 D128, bx=by=64, bigbird pattern, fp16
   ragged        block-sparse MHA, B2 N8 Sq=Skv=3000 D128, bx=48 by=80, Bernoulli(0.3)
                 with the diagonal forced on, fp16
 
 Packed variable-length sequences (``varlen_inputs``): q, dO [Hq, total, D], k, v
 [Hkv, total, D], sink [Hq] and cu_seqlens [B + 1] int32.  The pages' varlen row gives batch
-8, 64 heads, groups 16 (read as 16 query heads per K/V head: Hkv = 4) and 2048 tokens; the
-lengths are drawn uniformly from [max/2, max] (t = 6) with the first set to max.
+8, 64 heads, groups 16 (read as 16 query heads per K/V head: Hkv = 4) and 2048 tokens.
+Two batches (``VARLEN``): ``varlen_8x2048``, eight sequences of exactly 2048 tokens (the
+plain reading), and ``varlen_mixed``, lengths drawn uniformly from [1024, 2048] (t = 6)
+with the first set to 2048.
 
 Seeds: numpy ``default_rng(1000 * seed_base + t)`` with t = 0 for q, 1 k, 2 v, 3 dO,
 4 sink, 5 mask, 6 sequence lengths.  The bigbird reading: for query block i keep {i}, the global columns
@@ -79,6 +83,10 @@ WORKLOADS = {
                            seed_base=3),
     "large_causal": Workload("large_causal", SINK, 1, 64, 8, 8192, 8192, 128, torch.bfloat16, window=8192,
                              seed_base=3),
+    # The sink page's kernel-table shape (batch 1, 64 heads, groups of 8, 4096 tokens, d 128,
+    # fp16); the window is read as the whole sequence.
+    "pages_h64_s4096": Workload("pages_h64_s4096", SINK, 1, 64, 8, 4096, 4096, 128, torch.float16, window=4096,
+                                seed_base=120),
     "bigbird": Workload("bigbird", BLOCKSPARSE, 1, 16, 16, 8192, 8192, 128, torch.float16, bx=64, by=64,
                         pattern="bigbird", seed_base=4),
     "ragged": Workload("ragged", BLOCKSPARSE, 2, 8, 8, 3000, 3000, 128, torch.float16, bx=48, by=80,
@@ -204,3 +212,28 @@ def varlen_inputs(lengths, Hq, Hkv, dtype=torch.float16, D=128, seed_base=300):
         "cu_seqlens": torch.from_numpy(cu.astype(np.int32)),
         "max_seqlen": max(1, max(lengths)),
     }
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    lengths: tuple
+    Hq: int
+    Hkv: int
+    window: int
+    dtype: torch.dtype
+    seed_base: int
+    D: int = 128
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+    def inputs(self):
+        return varlen_inputs(list(self.lengths), self.Hq, self.Hkv, self.dtype, D=self.D, seed_base=self.seed_base)
+
+
+VARLEN = {
+    "varlen_8x2048": VarlenWorkload("varlen_8x2048", (2048,) * 8, 64, 4, 2048, torch.float16, 320),
+    "varlen_mixed": VarlenWorkload("varlen_mixed", tuple(varlen_lengths(8, 2048)), 64, 4, 2048, torch.float16, 300),
+}

@@ -170,3 +170,25 @@ def test_binding_fails_loudly_without_library(tmp_path):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "no fallback" in r.stderr
+
+
+def test_binding_rejects_bad_workspace():
+    """A caller-supplied workspace is checked before any pointer reaches the library: dtype,
+    device, contiguity and size (CPU tensors stand in for the wrong device here)."""
+    import torch
+    from masked_attention_backward_amd import api
+    dev = torch.device("cpu")
+    need = api.attn_sink_bwd_workspace_bytes(1, 4, 1, 128)
+    assert need > 0
+    ok = torch.empty(need, dtype=torch.uint8)
+    assert api._workspace(need, dev, ok) is ok
+    with pytest.raises(TypeError):
+        api._workspace(need, dev, torch.empty(need, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        api._workspace(need, dev, bytearray(need))
+    with pytest.raises(ValueError):
+        api._workspace(need, torch.device("cuda:0"), ok)
+    with pytest.raises(ValueError):
+        api._workspace(need, dev, torch.empty(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        api._workspace(need, dev, torch.empty(2 * need, dtype=torch.uint8)[::2])

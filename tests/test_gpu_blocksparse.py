@@ -206,17 +206,13 @@ def test_deterministic_and_fully_written():
 
 
 @pytest.mark.slow
-def test_bigbird_config_sampled():
+def test_bigbird_config_full():
+    """The bigbird configuration (B1 N16 S8192, bx = by = 64, fp16): every element of dQ, dK, dV."""
     wl = W.WORKLOADS["bigbird"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
     dq, dk, dv = gpu_bwd(wl, x)
-    rng = np.random.default_rng(9)
-    S = wl.Sq
-    rows = [0, 1, 63, 64, 65, 127, 128, 4095, S - 65, S - 64, S - 1] + list(rng.integers(0, S, 10))
-    qs = [(0, int(n), int(i)) for i in rows for n in (0, 9, 15)]
-    ks = [(0, int(n), int(j)) for j in rows for n in (0, 9, 15)]
-    ref = oracle.blocksparse_attention_backward_sampled(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"],
-                                                        x["block_mask"], wl.bx, wl.by, wl.scale, qs, ks)
-    check("dq[sampled]", torch.stack([dq[b, n, i] for b, n, i in qs]), ref["dq"], wl.dtype)
-    check("dk[sampled]", torch.stack([dk[b, n, j] for b, n, j in ks]), ref["dk"], wl.dtype)
-    check("dv[sampled]", torch.stack([dv[b, n, j] for b, n, j in ks]), ref["dv"], wl.dtype)
+    ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
+                                                wl.bx, wl.by, wl.scale)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)

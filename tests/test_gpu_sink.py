@@ -163,19 +163,52 @@ def test_large_window128_full():
 
 
 @pytest.mark.slow
-def test_large_causal_sampled():
-    """Full-size full-causal run (the benchmarked launch); outputs checked at sampled rows."""
+def test_large_causal_full():
+    """The benchmarked launch (B1 Hq64 Hkv8 S8192, window = S, bf16): every element of dQ, dK,
+    dV, dsink and Delta against the oracle."""
     wl = W.WORKLOADS["large_causal"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
-    rng = np.random.default_rng(7)
-    S = wl.Sq
-    rows = [0, 1, 63, 64, 127, 128, 4095, 4096, S - 129, S - 128, S - 1] + list(rng.integers(0, S, 10))
-    qs = [(0, int(h), int(i)) for i in rows for h in (0, 37, 63)]
-    ks = [(0, int(h), int(j)) for j in rows for h in (0, 5, 7)]
-    ref = oracle.sink_attention_backward_sampled(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"],
-                                                 wl.window, wl.scale, qs, ks)
+    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("delta", delta, ref["delta"], wl.dtype)
     check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq[sampled]", torch.stack([dq[b, h, i] for b, h, i in qs]), ref["dq"], wl.dtype)
-    check("dk[sampled]", torch.stack([dk[b, h, j] for b, h, j in ks]), ref["dk"], wl.dtype)
-    check("dv[sampled]", torch.stack([dv[b, h, j] for b, h, j in ks]), ref["dv"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)
+
+
+# The sink page's kernel-table shape: batch 1, 64 query heads, groups of 8 (8 K/V heads),
+# 4096 tokens, head dimension 128, fp16; the window is read as the whole sequence (causal).
+PAGES_SHAPE = W.WORKLOADS["pages_h64_s4096"]
+
+
+@pytest.mark.slow
+def test_pages_shape_forward_full():
+    """Forward at the sink page's table shape (the paired-tile dense forward: 32 tiles of 128
+    query rows per head, tile p with tile 31 - p): every O and lse element against the oracle."""
+    wl = PAGES_SHAPE
+    x = W.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    print(f"[gpu] attn_sink_fwd {wl.name}", flush=True)
+    o, lse = api().attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sink_attention_forward(x["q"], x["k"], x["v"], x["sink"], wl.window, wl.scale)
+    check("o", o, ro, wl.dtype)
+    err = np.abs(lse.cpu().double().numpy() - rl)
+    assert np.all(err <= 1e-5 + 1e-5 * np.abs(rl)), err.max()
+
+
+@pytest.mark.slow
+def test_pages_shape_backward_full():
+    """Backward at the sink page's table shape: every element of dQ, dK, dV, dsink, Delta."""
+    wl = PAGES_SHAPE
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check("delta", delta, ref["delta"], wl.dtype)
+    check("dsink", dsink, ref["dsink"], wl.dtype)
+    check("dq", dq, ref["dq"], wl.dtype)
+    check("dk", dk, ref["dk"], wl.dtype)
+    check("dv", dv, ref["dv"], wl.dtype)

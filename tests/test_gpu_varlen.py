@@ -197,3 +197,42 @@ def test_pages_varlen_forward_two_sequences():
                                                x["sink"], window, SCALE)
         check(f"o[seq {b}]", o[:, s0:s1], ro[0], dtype)
         check(f"lse[seq {b}]", lse[:, s0:s1], rl[0], dtype)
+
+
+@pytest.mark.slow
+def test_pages_varlen_equal_lengths_full():
+    """The sink page's varlen row under its plain reading: 8 sequences of exactly 2048 tokens,
+    64 query heads, 4 K/V heads, fp16, causal within each sequence.  Every element of dQ, dK,
+    dV and dsink against the dense oracle applied to each sequence (equal to the packed
+    definition on that sequence's rows; dsink sums over the sequences)."""
+    vw = W.VARLEN["varlen_8x2048"]
+    lengths, hq, hkv, dtype, window = list(vw.lengths), vw.Hq, vw.Hkv, vw.dtype, vw.window
+    x = vw.inputs()
+    cu = x["cu_seqlens"].numpy().astype(np.int64)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty(x["q"].shape[:2], dtype=torch.float32)
+    for b in range(len(lengths)):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        ob, lb = oracle.sink_attention_forward(x["q"][None, :, s0:s1], x["k"][None, :, s0:s1],
+                                               x["v"][None, :, s0:s1], x["sink"], window, SCALE)
+        o[:, s0:s1] = torch.from_numpy(ob[0]).to(dtype)
+        lse[:, s0:s1] = torch.from_numpy(lb[0]).to(torch.float32)
+    x["o"], x["lse"] = o, lse
+    dq, dk, dv, dsink = gpu_bwd("pages_varlen_8x2048", x, window)
+    dq_ref = np.zeros(tuple(x["q"].shape))
+    dk_ref = np.zeros(tuple(x["k"].shape))
+    dv_ref = np.zeros(tuple(x["v"].shape))
+    dsink_ref = np.zeros(hq)
+    for b in range(len(lengths)):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        sl = lambda t: t[None, :, s0:s1]
+        ref = oracle.sink_attention_backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["o"]), sl(x["do"]),
+                                             sl(x["lse"]), x["sink"], window, SCALE)
+        dq_ref[:, s0:s1] = ref["dq"][0]
+        dk_ref[:, s0:s1] = ref["dk"][0]
+        dv_ref[:, s0:s1] = ref["dv"][0]
+        dsink_ref += ref["dsink"]
+    check("dsink", dsink, dsink_ref, dtype)
+    check("dq", dq, dq_ref, dtype)
+    check("dk", dk, dk_ref, dtype)
+    check("dv", dv, dv_ref, dtype)
