@@ -67,7 +67,8 @@ enum {
   MA_EINVAL = 1,        /* null/misaligned pointer, non-positive size, Hq % Hkv != 0, window < 1, ... */
   MA_EUNSUPPORTED = 2,  /* D != 128, bx/by not a multiple of 16 or > 128, unknown dtype */
   MA_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() query */
-  MA_ELAUNCH = 4        /* the HIP runtime reported an error while enqueueing */
+  MA_ELAUNCH = 4,       /* the HIP runtime reported an error while enqueueing */
+  MA_ESCRATCH = 5       /* attn_sink_bwd_noalloc: the problem needs more than its static scratch */
 };
 
 /* Element types of the activation tensors. */
@@ -114,6 +115,28 @@ int attn_sink_bwd(const void* q, const void* k, const void* v,
                   void* workspace, size_t workspace_bytes,
                   int B, int Hq, int Hkv, int S, int D, int window, float scale,
                   int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * attn_sink_bwd_noalloc: attn_sink_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels, results and errors as attn_sink_bwd, without the workspace: its
+ * scratch (Delta, lse * log2 e, dsink partials; the attn_sink_bwd workspace layout) lives in
+ * a static device array of MA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * from the first call on that GPU until the process ends; its device address is looked up
+ * once per device.  The call allocates nothing and enqueues no memset (every scratch byte
+ * it reads is written earlier in the same call).
+ *   - MA_ESCRATCH when attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D) exceeds
+ *     MA_NOALLOC_SCRATCH_BYTES (nothing is enqueued).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind: calls
+ *     that overlap on one GPU (concurrent streams, or host threads) race and must be
+ *     serialised by the caller.
+ * --------------------------------------------------------------------------------- */
+#define MA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse, const float* sink,
+                          void* dq, void* dk, void* dv, float* dsink,
+                          int B, int Hq, int Hkv, int S, int D, int window, float scale,
+                          int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * (B) blocksparse_build_tables: device-side mask transpose and selection tables.

@@ -16,7 +16,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmaskattn.so")
 
 MA_F16, MA_BF16 = 0, 1
-STATUS = {0: "MA_OK", 1: "MA_EINVAL", 2: "MA_EUNSUPPORTED", 3: "MA_EWORKSPACE", 4: "MA_ELAUNCH"}
+STATUS = {0: "MA_OK", 1: "MA_EINVAL", 2: "MA_EUNSUPPORTED", 3: "MA_EWORKSPACE", 4: "MA_ELAUNCH", 5: "MA_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = (
     "maskattn_strerror",
@@ -33,6 +34,7 @@ EXPORTS = (
     "blocksparse_attn_bwd_gqa",
     "attn_sink_fwd_varlen",
     "attn_sink_bwd_varlen",
+    "attn_sink_bwd_noalloc",
 )
 
 
@@ -76,6 +78,8 @@ def _load():
     lib.attn_sink_fwd_varlen.restype = I
     lib.attn_sink_bwd_varlen.argtypes = [P] * 12 + [P, Z] + [I] * 7 + [F, I, P]
     lib.attn_sink_bwd_varlen.restype = I
+    lib.attn_sink_bwd_noalloc.argtypes = [P] * 11 + [I] * 6 + [F, I, P]
+    lib.attn_sink_bwd_noalloc.restype = I
     return lib
 
 
@@ -182,6 +186,30 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
         sp = (S + 63) // 64 * 64
         delta = ws[: B * Hq * sp * 4].view(torch.float32).view(B, Hq, sp)[..., :S]
         return dq, dk, dv, dsink, delta
+    return dq, dk, dv, dsink
+
+
+def attn_sink_bwd_noalloc(q, k, v, o, do, lse, sink, window, scale=None):
+    """attn_sink_bwd without a workspace: the library's static scratch array holds Delta, lse*log2e
+    and the dsink partials (calls that overlap on one GPU race) -> (dq, dk, dv, dsink)."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _need(t, name, (B, Hq, S, D), q.dtype, dev)
+    _need(k, "k", (B, Hkv, S, D), q.dtype, dev)
+    _need(v, "v", (B, Hkv, S, D), q.dtype, dev)
+    _need(lse, "lse", (B, Hq, S), torch.float32, dev)
+    _need(sink, "sink", (Hq,), torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsink = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    st = lib.attn_sink_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(sink), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(dsink), B, Hq, Hkv, S, D, int(window), scale,
+                                   _dtype_code(q), _stream(dev))
+    _check("attn_sink_bwd_noalloc", st)
     return dq, dk, dv, dsink
 
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "maskattn.h"
 #include "ma_launch.h"
 
@@ -111,6 +113,40 @@ int status_of(hipError_t e) { return e == hipSuccess ? MA_OK : MA_ELAUNCH; }
 
 }  // namespace
 
+// Scratch memory of attn_sink_bwd_noalloc (Delta, lse * log2 e and the dsink partials, laid
+// out as the attn_sink_bwd workspace): a file-scope device array, one copy per GPU, resident
+// from the first use of the library on that GPU until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it only names the symbol): the device
+// address is looked up once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) unsigned char scratch[MA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call per device,
+// with that device current).
+hipError_t scratch_address(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = r;
+    g_scratch_ptr[dev] = (r == hipSuccess) ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* maskattn_strerror(int status) {
@@ -120,6 +156,9 @@ const char* maskattn_strerror(int status) {
     case MA_EUNSUPPORTED: return "unsupported configuration (D != 128, block size, dtype or size limits)";
     case MA_EWORKSPACE: return "workspace too small";
     case MA_ELAUNCH: return "HIP runtime error while enqueueing";
+    case MA_ESCRATCH:
+      return "problem needs more scratch than attn_sink_bwd_noalloc's static array holds "
+             "(MA_NOALLOC_SCRATCH_BYTES); use attn_sink_bwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -205,6 +244,23 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const void*
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return MA_EINVAL;
   return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, workspace, workspace_bytes, B, Hq, Hkv, S, D,
                        window, scale, dtype, stream, events);
+}
+
+int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink, int B,
+                          int Hq, int Hkv, int S, int D, int window, float scale, int dtype, void* stream) {
+  const int st = check_common(B, Hq, Hkv, S, D, scale, dtype);
+  if (st) return st;
+  if (window < 1) return MA_EINVAL;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) || !tensor_ok(dq) ||
+      !tensor_ok(dk) || !tensor_ok(dv))
+    return MA_EINVAL;
+  if (!lse || !aligned(lse, 4) || !sink || !aligned(sink, 4) || !dsink || !aligned(dsink, 4)) return MA_EINVAL;
+  if (attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D) > (size_t)MA_NOALLOC_SCRATCH_BYTES) return MA_ESCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess || ws == nullptr) return MA_ELAUNCH;
+  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, ws, (size_t)MA_NOALLOC_SCRATCH_BYTES, B, Hq,
+                       Hkv, S, D, window, scale, dtype, stream, nullptr);
 }
 
 // Packed sequences: B sequences of at most max_seqlen rows at offsets cu_seqlens[0..B] of

@@ -40,8 +40,8 @@ def test_exports_match_header(lib):
 
 def test_strerror(lib):
     lib.maskattn_strerror.restype = ctypes.c_char_p
-    for s in range(5):
-        assert lib.maskattn_strerror(s)
+    for s in range(6):
+        assert lib.maskattn_strerror(s) and b"unknown" not in lib.maskattn_strerror(s)
     assert b"unknown" in lib.maskattn_strerror(99)
 
 
@@ -192,3 +192,31 @@ def test_binding_rejects_bad_workspace():
         api._workspace(need, dev, torch.empty(need - 1, dtype=torch.uint8))
     with pytest.raises(ValueError):
         api._workspace(need, dev, torch.empty(2 * need, dtype=torch.uint8)[::2])
+
+
+def sink_bwd_noalloc(lib, B=1, Hq=4, Hkv=1, S=128, D=128, window=64, scale=0.088, dtype=F16, **ptrs):
+    f = lib.attn_sink_bwd_noalloc
+    V, I = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [V] * 11 + [I] * 6 + [ctypes.c_float, I, V]
+    names = ["q", "k", "v", "o", "do", "lse", "sink", "dq", "dk", "dv", "dsink"]
+    vals = [ptrs.get(n, P) for n in names]
+    return f(*vals, B, Hq, Hkv, S, D, window, scale, dtype, None)
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free backward checks its arguments like attn_sink_bwd and refuses a problem
+    whose scratch exceeds the static array (MA_ESCRATCH = 5), all before any HIP call."""
+    ESCRATCH = 5
+    assert sink_bwd_noalloc(lib, q=0) == EINVAL
+    assert sink_bwd_noalloc(lib, dk=P + 8) == EINVAL
+    assert sink_bwd_noalloc(lib, dsink=0) == EINVAL
+    assert sink_bwd_noalloc(lib, window=0) == EINVAL
+    assert sink_bwd_noalloc(lib, Hq=3, Hkv=2) == EINVAL
+    assert sink_bwd_noalloc(lib, D=64) == EUNSUP
+    assert sink_bwd_noalloc(lib, dtype=7) == EUNSUP
+    lib.attn_sink_bwd_workspace_bytes.restype = ctypes.c_size_t
+    limit = 32 << 20
+    # 64 heads x 65536 rows: 2 x 16 MiB of per-row buffers plus the partials -> over the limit.
+    assert lib.attn_sink_bwd_workspace_bytes(1, 64, 8, 65536, 128) > limit
+    assert sink_bwd_noalloc(lib, Hq=64, Hkv=8, S=65536, window=65536) == ESCRATCH
+    assert lib.attn_sink_bwd_workspace_bytes(1, 64, 8, 8192, 128) <= limit
