@@ -53,6 +53,9 @@ KERNEL_SOURCES = ["attn_bwd_kernels.h", "attn_bwd.hip", "attn_bwd_variant.hip", 
 BOUND = {"tiny": "launch", "mid": "hbm", "large_w128": "hbm", "large_causal": "mfma", "bigbird": "hbm",
          "ragged": "mfma", "pages_h64_s4096": "mfma", "pages_h64_s4096_fwd": "mfma", "varlen_8x2048": "mfma",
          "varlen_mixed": "mfma"}
+# Sink path: workspace size that selects the dQ path ("ds_bank": the dK/dV kernel stores dS and
+# dQ is one GEMM per block; "recompute": the minimum workspace, dQ recomputes S and dP).
+DQ_PATH = "ds_bank"
 CONFIG_ORDER = ["tiny", "mid", "large_w128", "large_causal", "bigbird", "ragged", "pages_h64_s4096",
                 "pages_h64_s4096_fwd", "varlen_8x2048", "varlen_mixed"]
 
@@ -327,7 +330,8 @@ def make_case(name, dev):
         smax = g["max_seqlen"]
         o, lse = api.attn_sink_fwd_varlen(g["q"], g["k"], g["v"], g["sink"], g["cu_seqlens"], smax, vw.window, vw.scale)
         B, T = len(vw.lengths), sum(vw.lengths)
-        nbytes = api.attn_sink_bwd_workspace_bytes(B, vw.Hq, vw.Hkv, smax)
+        nbytes = (api.attn_sink_bwd_ds_workspace_bytes(B, vw.Hq, vw.Hkv, smax, vw.window) if DQ_PATH == "ds_bank"
+                  else api.attn_sink_bwd_workspace_bytes(B, vw.Hq, vw.Hkv, smax))
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
         dsink = torch.empty(vw.Hq, dtype=torch.float32, device=dev)
@@ -366,7 +370,8 @@ def make_case(name, dev):
                     dts, cfg)
     if wl.kind == "sink":
         o, lse = api.attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
-        nbytes = api.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq)
+        nbytes = (api.attn_sink_bwd_ds_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.window) if DQ_PATH == "ds_bank"
+                  else api.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq))
     else:
         o, lse = api.blocksparse_attn_fwd(g["q"], g["k"], g["v"], g["block_mask"], wl.bx, wl.by, wl.scale)
         nbytes = api.blocksparse_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv, wl.bx, wl.by)
@@ -469,6 +474,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration sweep")
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--calls", type=int, default=4, help="calls per configuration per round")
+    ap.add_argument("--dq-path", choices=["ds_bank", "recompute"], default="ds_bank",
+                    help="sink path: workspace size selecting how dQ is computed")
     ap.add_argument("--with-copy-probe", action="store_true",
                     help="also run one 256 MiB device-to-device copy (a kernel of known traffic, used to scale "
                          "hardware byte counters)")
@@ -484,6 +491,8 @@ def main():
         print(f"bench.py: unknown workload {args.workload!r}; one of {CONFIG_ORDER}", file=sys.stderr)
         sys.exit(2)
 
+    global DQ_PATH
+    DQ_PATH = args.dq_path
     import torch
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -523,7 +532,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": head.dtype,
         "data": "synthetic (seeded N(0,1) inputs; O, lse from the library forward)",
-        "config": head.config, "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
+        "config": head.config, "dq_path": DQ_PATH if head.kind in ("sink", "varlen") else None,
+        "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
         "counted_tflop": round(head.flops / 1e12, 4),
     }
 

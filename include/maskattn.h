@@ -100,6 +100,14 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
  *   2R:  dsink partials [B, Hq, ceil(S/64)] fp32 */
 size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
+/* Workspace bytes that select attn_sink_bwd's dS-bank path (0 on invalid sizes or window <
+ * 1): attn_sink_bwd_workspace_bytes() followed, at that offset, by the dS bank, 2048 bytes
+ * for every 32 x 32 (query block, key block) pair holding a visible (i, j) of each (batch,
+ * query head): B * Hq * sum_a (min(a, kb) + 1) blocks, a over ceil(S/32) query blocks, kb =
+ * ceil((min(window, S) - 1) / 32).  For window = S that is the lower triangle: 4.3 GB at
+ * B = 1, Hq = 64, S = 8192. */
+size_t attn_sink_bwd_ds_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int window);
+
 /* ---------------------------------------------------------------------------------
  * (A) attn_sink_bwd: backward pass with sink and sliding window.
  *   q, o, dout [B, Hq, S, D] dtype;  k, v [B, Hkv, S, D] dtype
@@ -107,6 +115,10 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
  *   sink [Hq] fp32
  *   dq [B, Hq, S, D], dk/dv [B, Hkv, S, D] dtype (out); dsink [Hq] fp32 (out)
  *   workspace: device buffer of >= attn_sink_bwd_workspace_bytes() bytes, 256-aligned.
+ *   With >= attn_sink_bwd_ds_workspace_bytes() bytes the dK/dV kernel also stores dS (in
+ *   the element type) and dQ is one GEMM per stored block; with less, the dQ kernel
+ *   recomputes S and dP.  The two paths round dS at different points, so their dQ may
+ *   differ in the last bits; both meet the same tolerance.
  * Results are deterministic: no atomics; every reduction has a fixed order.
  * --------------------------------------------------------------------------------- */
 int attn_sink_bwd(const void* q, const void* k, const void* v,
@@ -119,8 +131,10 @@ int attn_sink_bwd(const void* q, const void* k, const void* v,
 /* ---------------------------------------------------------------------------------
  * attn_sink_bwd_noalloc: attn_sink_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
- * Same arguments, kernels, results and errors as attn_sink_bwd, without the workspace: its
- * scratch (Delta, lse * log2 e, dsink partials; the attn_sink_bwd workspace layout) lives in
+ * Same arguments, results and errors as attn_sink_bwd given exactly
+ * attn_sink_bwd_workspace_bytes() of workspace (the path where dQ recomputes S and dP),
+ * without the workspace argument: its scratch (Delta, lse * log2 e, dsink partials; the
+ * attn_sink_bwd workspace layout) lives in
  * a static device array of MA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
  * from the first call on that GPU until the process ends; its device address is looked up
  * once per device.  The call allocates nothing and enqueues no memset (every scratch byte
@@ -230,7 +244,9 @@ int blocksparse_attn_bwd_gqa(const void* q, const void* k, const void* v,
  *   window counts within a sequence (window >= max_seqlen: causal within each sequence).
  *   dsink [Hq] fp32 (out): summed over all sequences.
  * Workspace: attn_sink_bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, D), same layout with S =
- * max_seqlen, per (sequence, head) (Delta row i of sequence b, head h at [b, h, i]).
+ * max_seqlen, per (sequence, head) (Delta row i of sequence b, head h at [b, h, i]);
+ * attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, max_seqlen, D, window) selects the dS-bank
+ * path as for attn_sink_bwd (bank entries per (sequence, head) sized for max_seqlen).
  * The offsets are device data and are not validated; the kernels clamp them to [0, total]
  * and each length to max_seqlen, so a table that breaks the contract gives unspecified
  * values but never an access outside the tensors.  Rows outside every sequence are not

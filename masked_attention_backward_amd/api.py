@@ -35,6 +35,7 @@ EXPORTS = (
     "attn_sink_fwd_varlen",
     "attn_sink_bwd_varlen",
     "attn_sink_bwd_noalloc",
+    "attn_sink_bwd_ds_workspace_bytes",
 )
 
 
@@ -80,6 +81,8 @@ def _load():
     lib.attn_sink_bwd_varlen.restype = I
     lib.attn_sink_bwd_noalloc.argtypes = [P] * 11 + [I] * 6 + [F, I, P]
     lib.attn_sink_bwd_noalloc.restype = I
+    lib.attn_sink_bwd_ds_workspace_bytes.argtypes = [I] * 6
+    lib.attn_sink_bwd_ds_workspace_bytes.restype = Z
     return lib
 
 
@@ -161,8 +164,14 @@ def attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D=128):
     return int(lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D))
 
 
+def attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, window, D=128):
+    return int(lib.attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, D, int(window)))
+
+
 def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None, return_delta=False):
-    """Backward with sink and sliding window -> (dq, dk, dv, dsink) [+ delta if return_delta]."""
+    """Backward with sink and sliding window -> (dq, dk, dv, dsink) [+ delta if return_delta].
+    Without a workspace one of attn_sink_bwd_ds_workspace_bytes() is allocated (the dS-bank
+    path); a caller workspace of attn_sink_bwd_workspace_bytes() selects the recompute path."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     dev = q.device
@@ -173,7 +182,8 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
     _need(lse, "lse", (B, Hq, S), torch.float32, dev)
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D), dev, workspace)
+    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D), dev, workspace) if workspace is not None \
+        else _workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, window, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -241,7 +251,8 @@ def attn_sink_fwd_varlen(q, k, v, sink, cu_seqlens, max_seqlen, window, scale=No
 
 
 def attn_sink_bwd_varlen(q, k, v, o, do, lse, sink, cu_seqlens, max_seqlen, window, scale=None, workspace=None):
-    """Backward over packed sequences (layouts as attn_sink_fwd_varlen) -> (dq, dk, dv, dsink)."""
+    """Backward over packed sequences (layouts as attn_sink_fwd_varlen) -> (dq, dk, dv, dsink);
+    workspace as attn_sink_bwd (dS-bank path by default)."""
     B, Hq, Hkv, total, D, smax, dev = _varlen_shapes(q, k, cu_seqlens, max_seqlen)
     for name, t in (("q", q), ("o", o), ("do", do)):
         _need(t, name, (Hq, total, D), q.dtype, dev)
@@ -250,7 +261,8 @@ def attn_sink_bwd_varlen(q, k, v, o, do, lse, sink, cu_seqlens, max_seqlen, wind
     _need(lse, "lse", (Hq, total), torch.float32, dev)
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D), dev, workspace)
+    ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D), dev, workspace) if workspace is not None \
+        else _workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, smax, window, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

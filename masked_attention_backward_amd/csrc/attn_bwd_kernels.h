@@ -166,11 +166,43 @@ struct DkdvShape {
   static constexpr int KV_TILES = NK <= 2 ? 1 : 2;   // 64-row tiles of K (and of V) in LDS
   static constexpr int KV_OFF = 2 * 2 * TILE_ELEMS;  // elements: two stages of (Q, dO) first
   static constexpr int ROWS_OFF = KV_OFF + 2 * KV_TILES * TILE_ELEMS;
-  static constexpr int SMEM_ELEMS = ROWS_OFF + 2 * 2 * 64 * 2;   // + 2 stages x (lse2, Delta) rows
+  static constexpr int ROWS_END = ROWS_OFF + 2 * 2 * 64 * 2;   // + 2 stages x (lse2, Delta) rows
+  // Window path with a dS bank: one 32 x 32 transpose area per wave (rows of 36 elements, 72 B).
+  static constexpr int DS_PITCH = 36;
+  static constexpr int DS_OFF = ROWS_END;
+  static constexpr int smem_elems(bool ds) { return ROWS_END + (ds ? NWAVES * 32 * DS_PITCH : 0); }
   static_assert(NK * 32 * 64 * 16 <= ROWS_OFF * 2, "partial-sum exchange must fit in the tile area");
 };
 
-template <class T, int MASK, int NK>
+// Transposes this wave's 32 x 32 dS block (held as two A operands of the dK product: lane
+// 32 h + c = key row c, da[t] = query rows 16 t + 8 (s / 4) + 4 h + s % 4) into the operand
+// order of the dQ product (lane 32 h + c = query row c, key rows in the same slot order):
+// out[t] is what the lane stores at bank entry + t * 1024 + 16 lane bytes.  The transpose
+// goes through a per-wave LDS area: row-major [key][query] writes, then column-taken reads
+// with ds_read_b64_tr_b16 (the pattern of frag_col).
+__device__ __forceinline__ void transpose_ds_block(const u32x4 (&da)[2], uint16_t* area, u32x4 (&out)[2], int lane) {
+  constexpr int P = 36;
+  const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st8(area + c * P + 16 * t + 4 * h, (u32x2){da[t][0], da[t][1]});
+    st8(area + c * P + 16 * t + 8 + 4 * h, (u32x2){da[t][2], da[t][3]});
+  }
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  const int rin = (lane & 15) >> 2;
+  const int cs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* r1 = area + (16 * t + 4 * h + rin) * P + cs;
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(r1));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(r1 + 8 * P));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    out[t] = (u32x4){xa[0], xa[1], ya[0], ya[1]};
+  }
+}
+
+template <class T, int MASK, int NK, bool DS = false>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kblock,
                                           uint16_t* smem, int chunk = 0, bool partial = false) {
   using Sh = DkdvShape<NK>;
@@ -278,11 +310,28 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     else
       return cur.bits == ~0ull;
   };
+  // dS bank: the previous tile's transposed block, stored after the next barrier (the block's
+  // address is wave-uniform; the lane adds 16 lane bytes).  The stores are non-temporal: the
+  // bank is read once, by the dQ kernel, and should not displace the query tiles the other
+  // workgroups of this kv head are still reading.
+  u32x4 ds_out[2];
+  long long ds_blk = -1;
+  auto flush_ds = [&]() {
+    if constexpr (MASK == MASK_WINDOW && DS) {
+      if (ds_blk >= 0) {
+        u32x4* p = reinterpret_cast<u32x4*>(a.ds_bank + ds_blk * 1024) + lane;
+        __builtin_nontemporal_store(ds_out[0], p);
+        __builtin_nontemporal_store(ds_out[1], p + 64);
+        ds_blk = -1;
+      }
+    }
+  };
   while (vcur) {
     const bool masked = !is_full();
     // This tile's loads (and, first time round, K/V) landed; the other stage is free.
     wait_vmcnt<0>();
     __syncthreads();
+    flush_ds();
     const int stg = it & 1;
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
 
@@ -398,6 +447,18 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       if constexpr (j < 4) srow(std::integral_constant<int, 9 + 2 * j>{});
       MA_STEP();
     });
+    if constexpr (MASK == MASK_WINDOW && DS) {
+      // This wave's block of the dS bank: query block 2 tile + qh, key block c0 / 32 + kb,
+      // stored when it holds a visible pair (the bank's band).  The store itself is issued
+      // after the next tile's barrier: stores count in vmcnt, and the wait at the top of the
+      // next tile must not wait for their completion.
+      const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
+      if (kbk <= qa && kbk >= band_lo(qa, a.ds_kb) && qa * 32 < sq) {
+        ds_blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + band_offset(qa, a.ds_kb) + kbk -
+                 band_lo(qa, a.ds_kb);
+        transpose_ds_block(da, smem + Sh::DS_OFF + wu * 32 * Sh::DS_PITCH, ds_out, lane);
+      }
+    }
     if (comp) {
       // Residual products of this tile: S and dP again from the stage (still resident), the
       // same mask and exponent, then dV += (P - hi(P))^T dO and dK += (dS - hi(dS))^T Q.
@@ -461,6 +522,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     cur = nxr;
     vcur = vn;
   }
+  flush_ds();
   wait_vmcnt<0>();   // K/V loads when there was no tile at all
   __syncthreads();
 
@@ -524,9 +586,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   }
 }
 
-template <class T, int MASK, int NK>
+template <class T, int MASK, int NK, bool DS = false>
 __global__ __launch_bounds__(2 * NK * 64) void dkdv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[DkdvShape<NK>::SMEM_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[DkdvShape<NK>::smem_elems(DS)];
   const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
@@ -540,10 +602,10 @@ __global__ __launch_bounds__(2 * NK * 64) void dkdv_kernel(const AttnArgs a) {
     const int nk = a.cu ? (seq_rows(a, b, a.Hkv, a.Skv).len + BC - 1) / BC : a.n_tiles;
     const int p2 = nk - 1 - p;
     if (a.pair && p > p2) return;
-    dkdv_tile<T, MASK, NK>(a, b, kvh, p * BC, a.Skv, 0, smem);
+    dkdv_tile<T, MASK, NK, DS>(a, b, kvh, p * BC, a.Skv, 0, smem);
     if (a.pair && p2 != p) {
       __syncthreads();
-      dkdv_tile<T, MASK, NK>(a, b, kvh, p2 * BC, a.Skv, 0, smem);
+      dkdv_tile<T, MASK, NK, DS>(a, b, kvh, p2 * BC, a.Skv, 0, smem);
     }
   } else {
     // p = (max_chunks - 1 - chunk) * nkb + key block: the last chunks, which only the most
@@ -782,15 +844,134 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------- dQ from the dS bank
+// Window path with a dS bank: dQ[q][d] = scale sum_k dS[q][k] K[k][d], one GEMM per live
+// 32 x 32 block, summed over the key blocks in ascending order (fixed, so results are
+// bit-identical run to run).  Workgroup = NW waves owning 32 NW consecutive query rows (wave w:
+// query block r0 / 32 + w); 64-row key tiles are staged in LDS (two stages of 16 KiB), the
+// dS fragments of the wave's live blocks go from HBM straight into registers, one tile ahead.
+// No softmax and no masking: masked entries of a stored block are exact zeros.
+template <class T, int NW>
+__device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, uint16_t* stages) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  q_end = min(q_end, sq);
+  if (r0 >= q_end) return;   // tile past the end of a shorter packed sequence (uniform)
+  const size_t qrow0 = qs.base + (size_t)hq * qs.head_stride;
+  const int kvh = hq / a.group;
+  const uint16_t* Kp = (const uint16_t*)a.k + (ks.base + (size_t)kvh * ks.head_stride) * HD;
+
+  // Key blocks of this wave (qa) and of the workgroup; 64-row key tiles [tlo, thi].
+  const int a0 = r0 >> 5, qa = a0 + wu;
+  const int a1 = min((q_end - 1) >> 5, a0 + NW - 1);
+  const bool rows = qa <= a1;
+  const int mlo = band_lo(qa, a.ds_kb), mhi = rows ? qa : -1;
+  const int tlo = band_lo(a0, a.ds_kb) >> 1, thi = a1 >> 1;
+  const uint16_t* bank = a.ds_bank + (((long long)b * a.Hq + hq) * a.ds_blocks + band_offset(qa, a.ds_kb) - mlo) * 1024 +
+                         lane * 8;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+  FragOff fo(lane);
+  // dS fragments of key tile t (two blocks, two k-steps each); zero outside the wave's band.
+  auto load_ds = [&](int t, u32x4 (&f)[2][2]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int kb = 2 * t + mb;
+      if (kb >= mlo && kb <= mhi) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(bank + (long long)kb * 1024);
+        f[mb][0] = __builtin_nontemporal_load(p);
+        f[mb][1] = __builtin_nontemporal_load(p + 64);
+      } else {
+        f[mb][0] = f[mb][1] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  u32x4 fa[2][2][2];
+  tile_load_async<NW>(stages_lds, Kp, tlo * 64, skv, wu, lane);
+  load_ds(tlo, fa[0]);
+  // One key tile: wait for its loads, free the other stage, issue the next tile's loads,
+  // then the GEMMs of the live blocks.
+  auto step = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 <= thi) {
+      tile_load_async<NW>(stages_lds + (uint32_t)((B ^ 1) * TILE_BYTES), Kp, (t + 1) * 64, skv, wu, lane);
+      load_ds(t + 1, fa[B ^ 1]);
+    }
+    const uint16_t* st = stages + B * TILE_ELEMS;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int kb = 2 * t + mb;
+      if (kb >= mlo && kb <= mhi) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa[B][mb][tt], frag_col(st, fo, 0, 2 * mb + tt, nb), acc[nb]);
+      }
+    }
+  };
+  for (int t = tlo; t <= thi; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 <= thi) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
+  uint16_t* dQp = (uint16_t*)a.dq + qrow0 * HD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
+    }
+  }
+}
+
+template <class T, int NW>
+__global__ __launch_bounds__(NW * 64, 4) void dq_ds_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[2 * TILE_ELEMS];
+  constexpr int BQ = 32 * NW;
+  int b, hq, p;
+  window_q_item(a, blockIdx.x, b, hq, p);
+  // Heaviest query tiles first; with `pair`, tile n - 1 - p also runs tile p (n counting the
+  // tiles of this sequence).
+  const int nq = a.cu ? (seq_rows(a, b, a.Hq, a.Sq).len + BQ - 1) / BQ : a.n_tiles;
+  const int t1 = nq - 1 - p;
+  if (t1 < 0 || (a.pair && p > t1)) return;
+  dq_ds_tile<T, NW>(a, b, hq, t1 * BQ, a.Sq, stages);
+  if (a.pair && p != t1) {
+    __syncthreads();
+    dq_ds_tile<T, NW>(a, b, hq, p * BQ, a.Sq, stages);
+  }
+}
+
 // Launch of one (element type, mask kind, NW) variant: dK/dV with 2 NW waves (NW key blocks
 // of 32 rows), dQ with NW waves (NW query blocks of 32 rows).
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
+  if constexpr (MASK == MASK_WINDOW) {
+    if (a.ds_bank) {
+      hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW, true>), dim3(grid), dim3(2 * NW * 64), 0, st, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(2 * NW * 64), 0, st, a);
 }
 
 template <class T, int MASK, int NW>
 inline void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
+  if constexpr (MASK == MASK_WINDOW) {
+    if (a.ds_bank) {
+      hipLaunchKernelGGL((dq_ds_kernel<T, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((dq_kernel<T, MASK, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
 }
 

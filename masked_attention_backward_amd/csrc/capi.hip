@@ -185,6 +185,20 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
   return align256(2 * rows + nblk * sizeof(float));
 }
 
+// dS bank of the window path: live 32 x 32 blocks per (sequence, query head), kb below the
+// diagonal for window W (clamped to S), 2048 bytes per block.
+static long long ds_kb_of(int S, int window) {
+  const int W = window < S ? window : S;
+  return (W - 1 + 31) / 32;
+}
+static long long ds_blocks_of(int S, int window) { return ma::band_offset((S + 31) / 32, ds_kb_of(S, window)); }
+
+size_t attn_sink_bwd_ds_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int window) {
+  const size_t base = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D);
+  if (base == 0 || window < 1) return 0;
+  return base + align256((size_t)B * Hq * (size_t)ds_blocks_of(S, window) * 2048);
+}
+
 static int sink_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink,
                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int window,
@@ -224,6 +238,13 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   a.cu = cu;
   a.total = total;
   a.window = window < S ? window : S;
+  // A workspace large enough for the dS bank selects the dQ path that reads the dS blocks the
+  // dK/dV kernel stores (one GEMM per block) instead of recomputing S and dP.
+  if (workspace_bytes >= attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, D, window)) {
+    a.ds_bank = at<uint16_t>(workspace, need);
+    a.ds_kb = (int)ds_kb_of(S, window);
+    a.ds_blocks = ds_blocks_of(S, window);
+  }
   e = ma::launch_window_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
   if (events) hipEventRecord((hipEvent_t)events[3], hs);
   return status_of(e);
@@ -256,11 +277,13 @@ int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v, const voi
       !tensor_ok(dk) || !tensor_ok(dv))
     return MA_EINVAL;
   if (!lse || !aligned(lse, 4) || !sink || !aligned(sink, 4) || !dsink || !aligned(dsink, 4)) return MA_EINVAL;
-  if (attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D) > (size_t)MA_NOALLOC_SCRATCH_BYTES) return MA_ESCRATCH;
+  const size_t need = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D);
+  if (need > (size_t)MA_NOALLOC_SCRATCH_BYTES) return MA_ESCRATCH;
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess || ws == nullptr) return MA_ELAUNCH;
-  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, ws, (size_t)MA_NOALLOC_SCRATCH_BYTES, B, Hq,
-                       Hkv, S, D, window, scale, dtype, stream, nullptr);
+  // Exactly the minimum workspace: the recompute dQ path, whatever the array could hold.
+  return sink_bwd_impl(q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, ws, need, B, Hq, Hkv, S, D, window, scale,
+                       dtype, stream, nullptr);
 }
 
 // Packed sequences: B sequences of at most max_seqlen rows at offsets cu_seqlens[0..B] of

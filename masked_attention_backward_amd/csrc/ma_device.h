@@ -166,6 +166,10 @@ struct AttnArgs {
   int max_chunks;        // block path: chunks per (kv head, key block) the grid provides for
   float* dkv_part;       // block path, chunked key blocks: fp32 partial dK (scaled) and dV,
                          // [2][B][Hkv][max_chunks][padded Skv][D]
+  uint16_t* ds_bank;     // window path: dS of every live 32 x 32 block, written by dK/dV and
+                         // read by the dQ GEMM (nullptr: dQ recomputes S and dP instead)
+  int ds_kb;             // window path: ceil((window - 1) / 32), live key blocks below the diagonal
+  long long ds_blocks;   // window path: live 32 x 32 blocks per (sequence, query head)
 };
 
 // Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per
@@ -188,5 +192,18 @@ __device__ __forceinline__ SeqRows seq_rows(const AttnArgs& a, int b, int H, int
 }
 
 enum { MASK_WINDOW = 0, MASK_BLOCK = 1 };
+
+// The dS bank (window path).  Query block a (rows 32a .. 32a + 31 of a sequence) sees key
+// blocks lo(a) = max(0, a - kb) .. a, kb = ceil((window - 1) / 32), exactly the blocks holding
+// a visible (q, k) pair.  A (sequence, head) stores them query block after query block, key
+// blocks ascending: block (a, b) is entry band_offset(a) + b - lo(a), 2048 bytes each, holding
+// the 16-bit dS[q][k] of the block as two dQ-operand fragments (k-steps t = 0, 1; 64 lanes x
+// 16 bytes each): lane 32 h + c holds dS[q = c][k = 16 t + 8 (s / 4) + 4 h + s % 4], s = 0..7,
+// the k-slot order of a column-taken key tile.
+__device__ __forceinline__ int band_lo(int a, int kb) { return max(0, a - kb); }
+__device__ __host__ __forceinline__ long long band_offset(long long a, long long kb) {
+  // sum over a' < a of (min(a', kb) + 1)
+  return a <= kb + 1 ? a * (a + 1) / 2 : (kb + 1) * (kb + 2) / 2 + (a - kb - 1) * (kb + 1);
+}
 
 }  // namespace ma

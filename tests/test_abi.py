@@ -93,6 +93,38 @@ def test_workspace_queries(lib):
     assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 144) == 0   # by > 128
 
 
+def brute_band_blocks(S, W):
+    """32 x 32 (query block, key block) pairs of one head holding a visible (i, j), 0 <= i - j < W."""
+    n = (S + 31) // 32
+    count = 0
+    for a in range(n):
+        for b in range(n):
+            i0, i1 = 32 * a, min(S, 32 * a + 32) - 1
+            j0, j1 = 32 * b, min(S, 32 * b + 32) - 1
+            if i1 - j0 >= 0 and i0 - j1 < W:   # some i - j in [0, W)
+                count += 1
+    return count
+
+
+def test_ds_workspace_query(lib):
+    """The dS-bank workspace: the minimum one plus 2048 bytes per live 32 x 32 block of every
+    (batch, query head), the block count checked against a brute-force scan of the band."""
+    Z, I = ctypes.c_size_t, ctypes.c_int
+    lib.attn_sink_bwd_workspace_bytes.restype = Z
+    lib.attn_sink_bwd_ds_workspace_bytes.restype = Z
+    lib.attn_sink_bwd_ds_workspace_bytes.argtypes = [I] * 6
+    for B, Hq, Hkv, S, W in [(1, 4, 1, 128, 64), (2, 32, 8, 2048, 128), (1, 2, 1, 1, 1), (3, 6, 3, 77, 5),
+                             (1, 8, 1, 300, 1), (1, 4, 4, 520, 300), (1, 2, 1, 64, 100000), (1, 64, 8, 8192, 8192)]:
+        base = lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, 128)
+        full = lib.attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, 128, W)
+        bank = B * Hq * brute_band_blocks(S, min(W, S)) * 2048
+        assert full == base + (bank + 255) // 256 * 256, (B, Hq, S, W)
+    assert lib.attn_sink_bwd_ds_workspace_bytes(1, 64, 8, 8192, 128, 8192) == \
+        lib.attn_sink_bwd_workspace_bytes(1, 64, 8, 8192, 128) + 64 * (256 * 257 // 2) * 2048
+    assert lib.attn_sink_bwd_ds_workspace_bytes(1, 4, 1, 128, 128, 0) == 0
+    assert lib.attn_sink_bwd_ds_workspace_bytes(1, 4, 1, 128, 64, 10) == 0
+
+
 def test_blocksparse_validation(lib):
     V, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     f = lib.blocksparse_attn_bwd

@@ -31,13 +31,35 @@ def with_oracle_forward(wl, x):
     return x
 
 
-def gpu_bwd(wl, x):
+PATHS = ("ds_bank", "recompute")
+
+
+def gpu_bwd(wl, x, path="ds_bank"):
+    """One backward call; `path` picks the workspace size: the dS-bank size (dK/dV stores dS,
+    dQ is one GEMM per block) or the minimum (dQ recomputes S and dP)."""
     g = {k: v.to(DEV) for k, v in x.items()}
-    print(f"[gpu] attn_sink_bwd {wl.name} B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} S{wl.Sq} W{wl.window} {wl.dtype}", flush=True)
-    out = api().attn_sink_bwd(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], wl.window, wl.scale,
-                              return_delta=True)
+    a = api()
+    print(f"[gpu] attn_sink_bwd ({path}) {wl.name} B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} S{wl.Sq} W{wl.window} {wl.dtype}",
+          flush=True)
+    ws = None
+    if path == "recompute":
+        ws = torch.empty(a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq), dtype=torch.uint8, device=DEV)
+    out = a.attn_sink_bwd(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], wl.window, wl.scale,
+                          workspace=ws, return_delta=True)
     torch.cuda.synchronize()
     return out
+
+
+def check_all(wl, x, ref, paths=PATHS, delta=True):
+    """Both dQ paths against the oracle: every element of dQ, dK, dV, dsink (and Delta)."""
+    for path in paths:
+        dq, dk, dv, dsink, dl = gpu_bwd(wl, x, path)
+        if delta:
+            check(f"{path} delta", dl, ref["delta"], wl.dtype)
+        check(f"{path} dsink", dsink, ref["dsink"], wl.dtype)
+        check(f"{path} dq", dq, ref["dq"], wl.dtype)
+        check(f"{path} dk", dk, ref["dk"], wl.dtype)
+        check(f"{path} dv", dv, ref["dv"], wl.dtype)
 
 
 SMALL = [
@@ -55,14 +77,9 @@ SMALL = [
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
 def test_bwd_small(wl):
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("delta", delta, ref["delta"], wl.dtype)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref)
 
 
 def test_bwd_no_sink_equals_causal():
@@ -71,26 +88,23 @@ def test_bwd_no_sink_equals_causal():
     x = W.make_inputs(wl)
     x["sink"] = torch.full((wl.Hq,), float("-inf"))
     x = with_oracle_forward(wl, x)
-    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    assert torch.all(dsink.cpu() == 0)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    for path in PATHS:
+        dq, dk, dv, dsink, _ = gpu_bwd(wl, x, path)
+        assert torch.all(dsink.cpu() == 0)
+        check(f"{path} dq", dq, ref["dq"], wl.dtype)
+        check(f"{path} dk", dk, ref["dk"], wl.dtype)
+        check(f"{path} dv", dv, ref["dv"], wl.dtype)
 
 
 def test_bwd_paired_tiles():
     """Wide window with enough heads that both kernels run tile p together with tile n-1-p."""
     wl = W.custom_sink("paired", 4, 16, 16, 1024, 1024, torch.float16, seed_base=111)
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref, delta=False)
 
 
 @pytest.mark.parametrize("wl", [SMALL[0], SMALL[2], SMALL[6], W.custom_sink("f_causal", 1, 4, 1, 333, 333,
@@ -111,17 +125,15 @@ def test_fwd(wl):
 def test_mid_config():
     wl = W.WORKLOADS["mid"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref)
 
 
-def test_deterministic_and_fully_written():
-    """Three runs are bit-identical, and outputs pre-filled with 0xFF (NaN) are fully overwritten."""
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic_and_fully_written(path):
+    """Three runs are bit-identical, and outputs and workspace pre-filled with 0xFF (NaN) are
+    fully overwritten / never read before written (both dQ paths)."""
     wl = W.custom_sink("det", 2, 8, 2, 333, 100, torch.bfloat16, seed_base=113)
     x = with_oracle_forward(wl, W.make_inputs(wl))
     g = {k: v.to(DEV) for k, v in x.items()}
@@ -132,7 +144,8 @@ def test_deterministic_and_fully_written():
         dk = torch.full_like(g["k"], float("nan"))
         dv = torch.full_like(g["v"], float("nan"))
         dsink = torch.full((wl.Hq,), float("nan"), device=DEV)
-        nbytes = a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq)
+        nbytes = (a.attn_sink_bwd_ds_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.window) if path == "ds_bank"
+                  else a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq))
         ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
         st = a.lib.attn_sink_bwd(*(ctypes.c_void_p(t.data_ptr()) for t in (
             g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], dq, dk, dv, dsink, ws)),
@@ -153,13 +166,9 @@ def test_deterministic_and_fully_written():
 def test_large_window128_full():
     wl = W.WORKLOADS["large_w128"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, _ = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref, delta=False)
 
 
 @pytest.mark.slow
@@ -168,14 +177,9 @@ def test_large_causal_full():
     dV, dsink and Delta against the oracle."""
     wl = W.WORKLOADS["large_causal"]
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("delta", delta, ref["delta"], wl.dtype)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref)
 
 
 # The sink page's kernel-table shape: batch 1, 64 query heads, groups of 8 (8 K/V heads),
@@ -204,11 +208,6 @@ def test_pages_shape_backward_full():
     """Backward at the sink page's table shape: every element of dQ, dK, dV, dsink, Delta."""
     wl = PAGES_SHAPE
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv, dsink, delta = gpu_bwd(wl, x)
     ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
                                          wl.scale)
-    check("delta", delta, ref["delta"], wl.dtype)
-    check("dsink", dsink, ref["dsink"], wl.dtype)
-    check("dq", dq, ref["dq"], wl.dtype)
-    check("dk", dk, ref["dk"], wl.dtype)
-    check("dv", dv, ref["dv"], wl.dtype)
+    check_all(wl, x, ref)

@@ -31,12 +31,20 @@ def with_oracle_forward(x, window, dtype):
     return x
 
 
-def gpu_bwd(name, x, window):
+def gpu_bwd(name, x, window, path="ds_bank"):
+    """One packed backward; `path` picks the workspace size as in the dense tests (the dS-bank
+    size, or the minimum: dQ recomputes S and dP)."""
     g = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
-    print(f"[gpu] attn_sink_bwd_varlen {name} Hq{x['q'].shape[0]} Hkv{x['k'].shape[0]} total{x['q'].shape[1]} "
-          f"max{x['max_seqlen']} W{window} {x['q'].dtype}", flush=True)
-    out = api().attn_sink_bwd_varlen(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], g["cu_seqlens"],
-                                     g["max_seqlen"], window, SCALE)
+    a = api()
+    print(f"[gpu] attn_sink_bwd_varlen ({path}) {name} Hq{x['q'].shape[0]} Hkv{x['k'].shape[0]} "
+          f"total{x['q'].shape[1]} max{x['max_seqlen']} W{window} {x['q'].dtype}", flush=True)
+    ws = None
+    if path == "recompute":
+        nb = len(x["cu_seqlens"]) - 1
+        ws = torch.empty(a.attn_sink_bwd_workspace_bytes(nb, x["q"].shape[0], x["k"].shape[0], x["max_seqlen"]),
+                         dtype=torch.uint8, device=DEV)
+    out = a.attn_sink_bwd_varlen(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], g["cu_seqlens"],
+                                 g["max_seqlen"], window, SCALE, workspace=ws)
     torch.cuda.synchronize()
     return out
 
@@ -58,13 +66,14 @@ SMALL = [
 def test_bwd_small(case):
     name, lengths, hq, hkv, window, dtype, seed = case
     x = with_oracle_forward(W.varlen_inputs(lengths, hq, hkv, dtype, seed_base=seed), window, dtype)
-    dq, dk, dv, dsink = gpu_bwd(name, x, window)
     ref = oracle.sink_attention_backward_varlen(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"],
                                                 x["cu_seqlens"].numpy(), window, SCALE)
-    check("dsink", dsink, ref["dsink"], dtype)
-    check("dq", dq, ref["dq"], dtype)
-    check("dk", dk, ref["dk"], dtype)
-    check("dv", dv, ref["dv"], dtype)
+    for path in ("ds_bank", "recompute"):
+        dq, dk, dv, dsink = gpu_bwd(name, x, window, path)
+        check(f"{path} dsink", dsink, ref["dsink"], dtype)
+        check(f"{path} dq", dq, ref["dq"], dtype)
+        check(f"{path} dk", dk, ref["dk"], dtype)
+        check(f"{path} dv", dv, ref["dv"], dtype)
 
 
 @pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda c: c[0])
@@ -218,7 +227,6 @@ def test_pages_varlen_equal_lengths_full():
         o[:, s0:s1] = torch.from_numpy(ob[0]).to(dtype)
         lse[:, s0:s1] = torch.from_numpy(lb[0]).to(torch.float32)
     x["o"], x["lse"] = o, lse
-    dq, dk, dv, dsink = gpu_bwd("pages_varlen_8x2048", x, window)
     dq_ref = np.zeros(tuple(x["q"].shape))
     dk_ref = np.zeros(tuple(x["k"].shape))
     dv_ref = np.zeros(tuple(x["v"].shape))
@@ -232,7 +240,9 @@ def test_pages_varlen_equal_lengths_full():
         dk_ref[:, s0:s1] = ref["dk"][0]
         dv_ref[:, s0:s1] = ref["dv"][0]
         dsink_ref += ref["dsink"]
-    check("dsink", dsink, dsink_ref, dtype)
-    check("dq", dq, dq_ref, dtype)
-    check("dk", dk, dk_ref, dtype)
-    check("dv", dv, dv_ref, dtype)
+    for path in ("ds_bank", "recompute"):
+        dq, dk, dv, dsink = gpu_bwd("pages_varlen_8x2048", x, window, path)
+        check(f"{path} dsink", dsink, dsink_ref, dtype)
+        check(f"{path} dq", dq, dq_ref, dtype)
+        check(f"{path} dk", dk, dk_ref, dtype)
+        check(f"{path} dv", dv, dv_ref, dtype)

@@ -1,5 +1,6 @@
 """The allocation-free backward (attn_sink_bwd_noalloc, scratch in the library's static device
-array) against attn_sink_bwd with a caller workspace, through the C ABI: two calls in a row,
+array) against attn_sink_bwd with a caller workspace of the minimum size (the same dQ path,
+where dQ recomputes S and dP), through the C ABI: two calls in a row,
 the second on a smaller problem, each compared bit for bit (same kernels, same order) and
 with outputs pre-filled with NaN so every element must be written."""
 
@@ -37,7 +38,10 @@ def test_noalloc_matches_workspace_call_twice():
         print(f"[gpu] attn_sink_fwd + attn_sink_bwd + attn_sink_bwd_noalloc {wl.name} B{wl.B} Hq{wl.Hq} "
               f"Hkv{wl.Hkv} S{wl.Sq} W{wl.window} {wl.dtype}", flush=True)
         o, lse = api.attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
-        want = api.attn_sink_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], wl.window, wl.scale)
+        ws = torch.empty(api.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq), dtype=torch.uint8,
+                         device=DEV)
+        want = api.attn_sink_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], wl.window, wl.scale,
+                                 workspace=ws)
         dq = torch.full_like(g["q"], float("nan"))
         dk = torch.full_like(g["k"], float("nan"))
         dv = torch.full_like(g["v"], float("nan"))
@@ -61,7 +65,8 @@ def test_noalloc_binding_and_scratch_limit():
     print(f"[gpu] attn_sink_bwd_noalloc binding {wl.name}", flush=True)
     o, lse = api.attn_sink_fwd(g["q"], g["k"], g["v"], g["sink"], wl.window, wl.scale)
     got = api.attn_sink_bwd_noalloc(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], wl.window, wl.scale)
-    want = api.attn_sink_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], wl.window, wl.scale)
+    ws = torch.empty(api.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq), dtype=torch.uint8, device=DEV)
+    want = api.attn_sink_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, g["sink"], wl.window, wl.scale, workspace=ws)
     torch.cuda.synchronize()
     for a, b in zip(got, want):
         assert torch.equal(_bits(a), _bits(b))
