@@ -160,52 +160,35 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Waves w and w + NK accumulate partial dK/dV of the same key rows over disjoint query rows;
 // the two partial sums are added through LDS at the end, in a fixed order (bit-identical
 // results run to run).
-template <int NK>
+template <int NK, int NSTAGE = 2>
 struct DkdvShape {
   static constexpr int NWAVES = 2 * NK;
-  static constexpr int KV_TILES = NK <= 2 ? 1 : 2;   // 64-row tiles of K (and of V) in LDS
-  static constexpr int KV_OFF = 2 * 2 * TILE_ELEMS;  // elements: two stages of (Q, dO) first
+  static constexpr int KV_TILES = NK <= 2 ? 1 : 2;        // 64-row tiles of K (and of V) in LDS
+  static constexpr int KV_OFF = NSTAGE * 2 * TILE_ELEMS;  // elements: the (Q, dO) stages first
   static constexpr int ROWS_OFF = KV_OFF + 2 * KV_TILES * TILE_ELEMS;
-  static constexpr int ROWS_END = ROWS_OFF + 2 * 2 * 64 * 2;   // + 2 stages x (lse2, Delta) rows
-  // Window path with a dS bank: one 32 x 32 transpose area per wave (rows of 36 elements, 72 B).
-  static constexpr int DS_PITCH = 36;
-  static constexpr int DS_OFF = ROWS_END;
-  static constexpr int smem_elems(bool ds) { return ROWS_END + (ds ? NWAVES * 32 * DS_PITCH : 0); }
+  static constexpr int ROWS_END = ROWS_OFF + NSTAGE * 2 * 64 * 2;   // + (lse2, Delta) rows per stage
+  static constexpr int smem_elems() { return ROWS_END; }
   static_assert(NK * 32 * 64 * 16 <= ROWS_OFF * 2, "partial-sum exchange must fit in the tile area");
 };
 
-// Transposes this wave's 32 x 32 dS block (held as two A operands of the dK product: lane
-// 32 h + c = key row c, da[t] = query rows 16 t + 8 (s / 4) + 4 h + s % 4) into the operand
-// order of the dQ product (lane 32 h + c = query row c, key rows in the same slot order):
-// out[t] is what the lane stores at bank entry + t * 1024 + 16 lane bytes.  The transpose
-// goes through a per-wave LDS area: row-major [key][query] writes, then column-taken reads
-// with ds_read_b64_tr_b16 (the pattern of frag_col).
-__device__ __forceinline__ void transpose_ds_block(const u32x4 (&da)[2], uint16_t* area, u32x4 (&out)[2], int lane) {
-  constexpr int P = 36;
-  const int c = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    st8(area + c * P + 16 * t + 4 * h, (u32x2){da[t][0], da[t][1]});
-    st8(area + c * P + 16 * t + 8 + 4 * h, (u32x2){da[t][2], da[t][3]});
-  }
-  typedef short short4v __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) short4v* lds_ptr;
-  const int rin = (lane & 15) >> 2;
-  const int cs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint16_t* r1 = area + (16 * t + 4 * h + rin) * P + cs;
-    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(r1));
-    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(r1 + 8 * P));
-    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
-    out[t] = (u32x4){xa[0], xa[1], ya[0], ya[1]};
-  }
-}
+// Stage count of the dK/dV pipeline.  Block path with key blocks of at most 64 rows: one
+// stage, so that two workgroups share a compute unit (two waves per SIMD; the loads of one
+// workgroup are hidden behind the other's matrix-core work, and so are the prologue and
+// epilogue of workgroups that walk only a few tiles).  Elsewhere two stages (the next tile's
+// loads are issued while the current one is computed).
+template <int MASK, int NK>
+constexpr int dkdv_stages() { return (MASK == MASK_BLOCK && NK <= 2) ? 1 : 2; }
+// Waves per SIMD the dK/dV kernel's register budget is sized for (the second argument of
+// __launch_bounds__ on this target): two for the one-stage variant (at most 256 registers per
+// lane); the eight-wave workgroups of the other variants imply two by themselves.
+template <int MASK, int NK>
+constexpr int dkdv_waves_per_simd() { return dkdv_stages<MASK, NK>() == 1 ? 2 : 1; }
 
 template <class T, int MASK, int NK, bool DS = false>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kblock,
                                           uint16_t* smem, int chunk = 0, bool partial = false) {
-  using Sh = DkdvShape<NK>;
+  constexpr int NSTAGE = dkdv_stages<MASK, NK>();
+  using Sh = DkdvShape<NK, NSTAGE>;
   constexpr int NWV = Sh::NWAVES;
   constexpr int BC = 32 * NK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
@@ -268,12 +251,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     if (wu == NWV - 1) row_load_async(rows + 256, a.delta + qhead * sq_pad + r.tile * 64, lane);
   };
 
-  // Negate V in LDS once it has landed (sign bit of every 16-bit element): dP is then
-  // accumulated as Delta + dO (-V)^T = Delta - dP, starting from the staged Delta rows, and
-  // dS = P (dP - Delta) = -(P (Delta - dP)) costs no subtraction.
-  wait_vmcnt<0>();
-  __syncthreads();
-  {
+  // V is negated in LDS once it has landed (sign bit of every 16-bit element), right after
+  // the first tile's barrier: dP is then accumulated as Delta + dO (-V)^T = Delta - dP,
+  // starting from the staged Delta rows, and dS = P (dP - Delta) = -(P (Delta - dP)) costs no
+  // subtraction.  The first tiles' loads go out together with K and V.
+  auto negate_v = [&]() {
     u32x4* vt = reinterpret_cast<u32x4*>(kvs + Sh::KV_TILES * TILE_ELEMS);
     constexpr int NCH = Sh::KV_TILES * TILE_BYTES / 16;   // 16-byte chunks of V
     for (int ch = tid; ch < NCH; ch += NWV * 64) {
@@ -281,8 +263,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       x ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       vt[ch] = x;
     }
-  }
-  __syncthreads();
+  };
 
   const float sl2 = a.scale_log2;
   const int kj = c0 + 32 * kb + c;
@@ -300,7 +281,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   TileRef cur{};
   bool vcur = fetch(cur);
   if (vcur) issue(cur, 0);
-  int it = 0;
+  int it = 0, stg = 0;
   // Tiles where every (q, kv) of the workgroup is visible need no mask (rows past the
   // sequence end need none either: lse2 = +inf there; key columns past the end are never
   // stored).
@@ -310,10 +291,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     else
       return cur.bits == ~0ull;
   };
-  // dS bank: the previous tile's transposed block, stored after the next barrier (the block's
-  // address is wave-uniform; the lane adds 16 lane bytes).  The stores are non-temporal: the
-  // bank is read once, by the dQ kernel, and should not displace the query tiles the other
-  // workgroups of this kv head are still reading.
+  // dS bank: the previous tile's block as this wave holds it (the two dK-product A operands),
+  // stored after the next barrier (the block's address is wave-uniform; the lane adds 16 lane
+  // bytes).  The stores are non-temporal: the bank is read once, by the dQ kernel, and should
+  // not displace the query tiles the other workgroups of this kv head are still reading.
   u32x4 ds_out[2];
   long long ds_blk = -1;
   auto flush_ds = [&]() {
@@ -328,11 +309,15 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   };
   while (vcur) {
     const bool masked = !is_full();
-    // This tile's loads (and, first time round, K/V) landed; the other stage is free.
+    // This tile's loads (and, first time round, K/V) landed; with two stages the other stage
+    // is free once every wave has passed the barrier.
     wait_vmcnt<0>();
     __syncthreads();
+    if (it == 0) {
+      negate_v();
+      __syncthreads();
+    }
     flush_ds();
-    const int stg = it & 1;
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
 
     // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
@@ -356,7 +341,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
     TileRef nxr{};
     const bool vn = fetch(nxr);
-    if (vn) issue(nxr, (it + 1) & 1);
+    if constexpr (NSTAGE == 2) {
+      if (vn) issue(nxr, stg ^ 1);
+    }
     MA_STEP();
     static_for<0, 8>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
@@ -456,7 +443,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       if (kbk <= qa && kbk >= band_lo(qa, a.ds_kb) && qa * 32 < sq) {
         ds_blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + band_offset(qa, a.ds_kb) + kbk -
                  band_lo(qa, a.ds_kb);
-        transpose_ds_block(da, smem + Sh::DS_OFF + wu * 32 * Sh::DS_PITCH, ds_out, lane);
+        ds_out[0] = da[0];
+        ds_out[1] = da[1];
       }
     }
     if (comp) {
@@ -513,14 +501,21 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
         dk[nb] = T::mma(dl[t], frag_col(stages, fo, 0, t, nb), dk[nb]);
       }
     }
+    if constexpr (NSTAGE == 2) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      fo.row[i] ^= STAGE_BYTES;
-      fo.col[i] ^= STAGE_BYTES;
+      for (int i = 0; i < 8; ++i) {
+        fo.row[i] ^= STAGE_BYTES;
+        fo.col[i] ^= STAGE_BYTES;
+      }
+      stg ^= 1;
+    } else {
+      // One stage: every wave is done reading it before the next tile's loads overwrite it.
+      __syncthreads();
+      if (vn) issue(nxr, 0);
     }
-    ++it;
     cur = nxr;
     vcur = vn;
+    ++it;
   }
   flush_ds();
   wait_vmcnt<0>();   // K/V loads when there was no tile at all
@@ -587,8 +582,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
 }
 
 template <class T, int MASK, int NK, bool DS = false>
-__global__ __launch_bounds__(2 * NK * 64) void dkdv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[DkdvShape<NK>::smem_elems(DS)];
+__global__ __launch_bounds__(2 * NK * 64, (dkdv_waves_per_simd<MASK, NK>())) void dkdv_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[DkdvShape<NK, dkdv_stages<MASK, NK>()>::smem_elems()];
   const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;
@@ -711,9 +706,16 @@ __device__ __forceinline__ void dq_compute(f32x16* acc, const FragOff& fo, const
   dqb(I1{}, none);
 }
 
+// Stage count of the dQ pipeline: on the block path with query blocks of at most 64 rows one
+// stage of K/V, so that four workgroups share a compute unit (two waves per SIMD); two stages
+// elsewhere (two workgroups per compute unit).
+template <int MASK, int NW>
+constexpr int dq_stages() { return (MASK == MASK_BLOCK && NW <= 2) ? 1 : 2; }
+
 template <class T, int MASK, int NW>
 __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, int qb,
                                          uint16_t* stages) {
+  constexpr int NS = dq_stages<MASK, NW>();
   constexpr int BQ = 32 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -789,14 +791,22 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     __syncthreads();
     TileRef nx{};
     const bool vn = fetch(nx);
-    if (vn) issue(nx.tile, (it + 1) & 1);
+    if constexpr (NS == 2) {
+      if (vn) issue(nx.tile, (it + 1) & 1);
+    }
     const int kdiff = qi - cur.tile * 64 - 4 * h;
     const uint64_t hbits = h ? (cur.bits >> 4) : cur.bits;
     dq_compute<T, MASK>(acc, fo, qf, of, stages, sl2, l2, dd, kdiff, a.window, hbits, masked);
+    if constexpr (NS == 2) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      fo.row[i] ^= STAGE_BYTES;
-      fo.col[i] ^= STAGE_BYTES;
+      for (int i = 0; i < 8; ++i) {
+        fo.row[i] ^= STAGE_BYTES;
+        fo.col[i] ^= STAGE_BYTES;
+      }
+    } else {
+      // One stage: every wave is done reading it before the next tile's loads overwrite it.
+      __syncthreads();
+      if (vn) issue(nx.tile, 0);
     }
     ++it;
     cur = nx;
@@ -818,7 +828,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
 
 template <class T, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[2 * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stages[dq_stages<MASK, NW>() * 2 * TILE_ELEMS];
   const int wg = blockIdx.x;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BQ = 32 * NW;
@@ -848,14 +858,32 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
 // Window path with a dS bank: dQ[q][d] = scale sum_k dS[q][k] K[k][d], one GEMM per live
 // 32 x 32 block, summed over the key blocks in ascending order (fixed, so results are
 // bit-identical run to run).  Workgroup = NW waves owning 32 NW consecutive query rows (wave w:
-// query block r0 / 32 + w); 64-row key tiles are staged in LDS (two stages of 16 KiB), the
-// dS fragments of the wave's live blocks go from HBM straight into registers, one tile ahead.
+// query block r0 / 32 + w).  Per 64-row key tile, one LDS stage holds the key tile and the two
+// dS blocks of every wave, all copied straight from HBM (LDS DMA), DQS_STAGES - 1 tiles ahead.
 // No softmax and no masking: masked entries of a stored block are exact zeros.
+//
+// A bank block holds dS as the dK/dV kernel's wave had it (lane 32 x + k: key k, slots s =
+// query 16 u + 8 (s / 4) + 4 x + s % 4 of 1 KiB unit u); the dQ product needs it the other way
+// round (lane = query row, slots = keys).  The transpose is one ds_read_b64_tr_b16 pair per
+// k-step: in a 16-lane group, lane 4 r + a addresses the 8 bytes holding the four queries
+// 16 u + 4 a + (0..3) of key k0 + r, and lane j receives query 16 u + j of keys k0 + (0..3).
+// The copies place logical 16-byte chunk L = 32 x + 4 m + r (m = key / 4) of unit u at slot
+//   P = 16 (m / 2) + 8 (u ^ (m % 2)) + 4 x + r,
+// so that the 32 lanes of each half-wave read 32 distinct 8-byte bank pairs.
+constexpr int DQS_STAGES = 2;
+
+template <int NW>
+struct DqDsShape {
+  static constexpr int STAGE_B = TILE_BYTES + NW * 4096;   // key tile, then 2 dS blocks per wave
+  static constexpr int elems() { return DQS_STAGES * STAGE_B / 2; }
+};
+
 template <class T, int NW>
-__device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, uint16_t* stages) {
+__device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, uint16_t* smem) {
+  using Sh = DqDsShape<NW>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const uint32_t stages_lds = __builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
   const int sq = qs.len, skv = ks.len;
   q_end = min(q_end, sq);
@@ -870,55 +898,83 @@ __device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int
   const bool rows = qa <= a1;
   const int mlo = band_lo(qa, a.ds_kb), mhi = rows ? qa : -1;
   const int tlo = band_lo(a0, a.ds_kb) >> 1, thi = a1 >> 1;
-  const uint16_t* bank = a.ds_bank + (((long long)b * a.Hq + hq) * a.ds_blocks + band_offset(qa, a.ds_kb) - mlo) * 1024 +
-                         lane * 8;
+  // Bank entry of key block kb is bank + kb * 1024 elements for kb in [mlo, mhi]; waves without
+  // rows copy the head's first block (never read).
+  const uint16_t* bank =
+      a.ds_bank + (((long long)b * a.Hq + hq) * a.ds_blocks + (rows ? band_offset(qa, a.ds_kb) - mlo : 0)) * 1024;
+
+  // Copy sources: the lane filling slot P of unit u fetches logical chunk L(P, u).
+  auto src_chunk = [&](int u) -> uint32_t {
+    const int m = 2 * (lane >> 4) + (((lane >> 3) & 1) ^ u);
+    return (uint32_t)(u * 1024 + (32 * ((lane >> 2) & 1) + 4 * m + (lane & 3)) * 16);
+  };
+  const uint32_t so0 = src_chunk(0), so1 = src_chunk(1);
+  // Transposing reads: byte offset of this lane's 8 bytes for k-step 0 (first slot quad) of a
+  // block; + 512 per k-step, + 256 for the second slot quad.
+  const int g = (lane >> 4) & 1, ia = lane & 3, ir = (lane >> 2) & 3;
+  const int dso = g * 1024 + 128 * (g ^ h) + 64 * (ia & 1) + 16 * ir + 8 * (ia >> 1);
+
+  auto issue = [&](int t, int s) {
+    const uint32_t st = smem_lds + (uint32_t)(s * Sh::STAGE_B);
+    tile_load_async<NW>(st, Kp, t * 64, skv, wu, lane);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int kb = rows ? min(max(2 * t + mb, mlo), mhi) : 0;
+      const uint16_t* blk = bank + (long long)kb * 1024;
+      const uint32_t d = st + (uint32_t)(TILE_BYTES + wu * 4096 + mb * 2048);
+      dma16(blk, so0, __builtin_amdgcn_readfirstlane(d));
+      dma16(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+    }
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
   FragOff fo(lane);
-  // dS fragments of key tile t (two blocks, two k-steps each); zero outside the wave's band.
-  auto load_ds = [&](int t, u32x4 (&f)[2][2]) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int kb = 2 * t + mb;
-      if (kb >= mlo && kb <= mhi) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(bank + (long long)kb * 1024);
-        f[mb][0] = __builtin_nontemporal_load(p);
-        f[mb][1] = __builtin_nontemporal_load(p + 64);
-      } else {
-        f[mb][0] = f[mb][1] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  auto ds_frag = [&](const char* blk, int tt) -> u32x4 {
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt + 256));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    return (u32x4){xa[0], xa[1], ya[0], ya[1]};
   };
-  u32x4 fa[2][2][2];
-  tile_load_async<NW>(stages_lds, Kp, tlo * 64, skv, wu, lane);
-  load_ds(tlo, fa[0]);
-  // One key tile: wait for its loads, free the other stage, issue the next tile's loads,
-  // then the GEMMs of the live blocks.
-  auto step = [&](auto bc, int t) {
-    constexpr int B = decltype(bc)::value;
-    wait_vmcnt<0>();
+
+  // Loads of the first DQS_STAGES - 1 tiles; then per tile: wait for its loads (the later
+  // tiles' 2 * (16 / NW + 4) copies per wave may stay in flight), barrier, issue the loads of
+  // the tile DQS_STAGES - 1 ahead into the stage freed by the barrier, multiply.
+  constexpr int PER_TILE = (16 + NW - 1) / NW + 4;   // copies per wave per tile (NW divides 16)
+  static_assert(16 % NW == 0, "key tile copies must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < DQS_STAGES - 1; ++j)
+    if (tlo + j <= thi) issue(tlo + j, j);
+  int s = 0;
+  for (int t = tlo; t <= thi; ++t) {
+    const int ahead = min(thi - t, DQS_STAGES - 2);   // tiles after t already issued
+    if constexpr (DQS_STAGES == 2) {
+      wait_vmcnt<0>();
+    } else {
+      if (ahead <= 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<PER_TILE>();
+      else wait_vmcnt<2 * PER_TILE>();
+    }
     __syncthreads();
-    if (t + 1 <= thi) {
-      tile_load_async<NW>(stages_lds + (uint32_t)((B ^ 1) * TILE_BYTES), Kp, (t + 1) * 64, skv, wu, lane);
-      load_ds(t + 1, fa[B ^ 1]);
-    }
-    const uint16_t* st = stages + B * TILE_ELEMS;
+    if (t + DQS_STAGES - 1 <= thi) issue(t + DQS_STAGES - 1, s == 0 ? DQS_STAGES - 1 : s - 1);
+    const uint16_t* kt = smem + s * (Sh::STAGE_B / 2);
+    const char* dsb = reinterpret_cast<const char*>(smem) + s * Sh::STAGE_B + TILE_BYTES + wu * 4096;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int kb = 2 * t + mb;
       if (kb >= mlo && kb <= mhi) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+          const u32x4 fa = ds_frag(dsb + mb * 2048, tt);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa[B][mb][tt], frag_col(st, fo, 0, 2 * mb + tt, nb), acc[nb]);
+          for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa, frag_col(kt, fo, 0, 2 * mb + tt, nb), acc[nb]);
+        }
       }
     }
-  };
-  for (int t = tlo; t <= thi; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 <= thi) step(std::integral_constant<int, 1>{}, t + 1);
+    s = s == DQS_STAGES - 1 ? 0 : s + 1;
   }
 
   // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
@@ -934,8 +990,8 @@ __device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int
 }
 
 template <class T, int NW>
-__global__ __launch_bounds__(NW * 64, 4) void dq_ds_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t stages[2 * TILE_ELEMS];
+__global__ __launch_bounds__(NW * 64, 2) void dq_ds_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[DqDsShape<NW>::elems()];
   constexpr int BQ = 32 * NW;
   int b, hq, p;
   window_q_item(a, blockIdx.x, b, hq, p);
@@ -944,10 +1000,10 @@ __global__ __launch_bounds__(NW * 64, 4) void dq_ds_kernel(const AttnArgs a) {
   const int nq = a.cu ? (seq_rows(a, b, a.Hq, a.Sq).len + BQ - 1) / BQ : a.n_tiles;
   const int t1 = nq - 1 - p;
   if (t1 < 0 || (a.pair && p > t1)) return;
-  dq_ds_tile<T, NW>(a, b, hq, t1 * BQ, a.Sq, stages);
+  dq_ds_tile<T, NW>(a, b, hq, t1 * BQ, a.Sq, smem);
   if (a.pair && p != t1) {
     __syncthreads();
-    dq_ds_tile<T, NW>(a, b, hq, p * BQ, a.Sq, stages);
+    dq_ds_tile<T, NW>(a, b, hq, p * BQ, a.Sq, smem);
   }
 }
 
