@@ -291,22 +291,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     else
       return cur.bits == ~0ull;
   };
-  // dS bank: the previous tile's block as this wave holds it (the two dK-product A operands),
-  // stored after the next barrier (the block's address is wave-uniform; the lane adds 16 lane
-  // bytes).  The stores are non-temporal: the bank is read once, by the dQ kernel, and should
-  // not displace the query tiles the other workgroups of this kv head are still reading.
-  u32x4 ds_out[2];
-  long long ds_blk = -1;
-  auto flush_ds = [&]() {
-    if constexpr (MASK == MASK_WINDOW && DS) {
-      if (ds_blk >= 0) {
-        u32x4* p = reinterpret_cast<u32x4*>(a.ds_bank + ds_blk * 1024) + lane;
-        __builtin_nontemporal_store(ds_out[0], p);
-        __builtin_nontemporal_store(ds_out[1], p + 64);
-        ds_blk = -1;
-      }
-    }
-  };
   while (vcur) {
     const bool masked = !is_full();
     // This tile's loads (and, first time round, K/V) landed; with two stages the other stage
@@ -317,7 +301,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       negate_v();
       __syncthreads();
     }
-    flush_ds();
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
 
     // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
@@ -402,6 +385,21 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, s[r]);
     const bool comp = __builtin_amdgcn_ballot_w64(lmax > -2.0f) != 0;
     MA_STEP();
+    // dS bank (window path): this wave's block, query block 2 tile + qh and key block
+    // c0 / 32 + kb, is stored when it holds a visible pair (the bank's band), as this wave
+    // holds it: the two A operands of the dK product, each stored as soon as it is packed, so
+    // that the stores complete under this tile's remaining MFMAs (stores count in vmcnt, which
+    // the next tile's first wait drains).  Non-temporal: the bank is read once, by the dQ
+    // kernel, and should not displace the query tiles the other workgroups still read.
+    bool ds_live = false;   // wave-uniform
+    u32x4* ds_dst = nullptr;
+    if constexpr (MASK == MASK_WINDOW && DS) {
+      const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
+      ds_live = kbk <= qa && kbk >= band_lo(qa, a.ds_kb) && qa * 32 < sq;
+      const long long blk =
+          ((long long)b * a.Hq + cur.head) * a.ds_blocks + band_offset(qa, a.ds_kb) + kbk - band_lo(qa, a.ds_kb);
+      ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
+    }
     // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
     // done one per MFMA between those eight MFMAs.
     u32x4 pa[2], da[2];
@@ -419,6 +417,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       }
     };
     static_for<0, 8>(srow);
+    if constexpr (MASK == MASK_WINDOW && DS) {
+      if (ds_live) __builtin_nontemporal_store(da[0], ds_dst);
+    }
     // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows.
     MA_STEP();
     static_for<0, 8>([&](auto jc) {
@@ -432,21 +433,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       MA_STEP();
       dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
       if constexpr (j < 4) srow(std::integral_constant<int, 9 + 2 * j>{});
+      if constexpr (MASK == MASK_WINDOW && DS && j == 3) {
+        if (ds_live) __builtin_nontemporal_store(da[1], ds_dst + 64);
+      }
       MA_STEP();
     });
-    if constexpr (MASK == MASK_WINDOW && DS) {
-      // This wave's block of the dS bank: query block 2 tile + qh, key block c0 / 32 + kb,
-      // stored when it holds a visible pair (the bank's band).  The store itself is issued
-      // after the next tile's barrier: stores count in vmcnt, and the wait at the top of the
-      // next tile must not wait for their completion.
-      const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
-      if (kbk <= qa && kbk >= band_lo(qa, a.ds_kb) && qa * 32 < sq) {
-        ds_blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + band_offset(qa, a.ds_kb) + kbk -
-                 band_lo(qa, a.ds_kb);
-        ds_out[0] = da[0];
-        ds_out[1] = da[1];
-      }
-    }
     if (comp) {
       // Residual products of this tile: S and dP again from the stage (still resident), the
       // same mask and exponent, then dV += (P - hi(P))^T dO and dK += (dS - hi(dS))^T Q.
@@ -517,7 +508,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     vcur = vn;
     ++it;
   }
-  flush_ds();
   wait_vmcnt<0>();   // K/V loads when there was no tile at all
   __syncthreads();
 
