@@ -86,7 +86,7 @@ struct BlockSource {
 // A workgroup may take only a chunk of that concatenated list: entries [first, first + count).
 struct BlockGroupSource {
   const int* sel_k = nullptr;   // [B, Hq, nkb, nqb]
-  const int* cnt_k = nullptr;   // [B, Hq, nkb]
+  const_int_ptr cnt_k = nullptr;   // [B, Hq, nkb] (scalar loads, see TileWalker)
   size_t row0 = 0;              // (b * Hq) * nkb + kblock: table row of query head 0
   int nkb = 0, nqb = 0, bx = 1, sq = 1;
   int head = 0, hend = 0;
@@ -94,7 +94,7 @@ struct BlockGroupSource {
   TileWalker walk{nullptr, 0, 1, 1};
   __device__ void init(const AttnArgs& a, int b, int kvh, int kblock, int first, int count) {
     sel_k = a.sel_k;
-    cnt_k = a.cnt_k;
+    cnt_k = (const_int_ptr)a.cnt_k;
     row0 = (size_t)b * a.Hq * a.nkb + kblock;
     nkb = a.nkb;
     nqb = a.nqb;
@@ -132,7 +132,8 @@ __device__ __forceinline__ int block_chunks(const AttnArgs& a, int b, int kvh, i
   if (a.chunk <= 0) return 1;
   const size_t row0 = ((size_t)b * a.Hq + (size_t)kvh * a.group) * a.nkb + kblock;
   int e = 0;
-  for (int h = 0; h < a.group; ++h) e += a.cnt_k[row0 + (size_t)h * a.nkb];
+  const_int_ptr cnt = (const_int_ptr)a.cnt_k;
+  for (int h = 0; h < a.group; ++h) e += cnt[row0 + (size_t)h * a.nkb];
   return max(1, (e + a.chunk - 1) / a.chunk);
 }
 
@@ -747,7 +748,7 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
     wsrc = WindowSource::make(0, 1, tlo, max(0, thi - tlo));
   } else {
     const size_t row = qhead * a.nqb + qb;
-    bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv), 0};
+    bsrc = BlockSource{TileWalker(a.sel_q + row * a.nkb, ((const_int_ptr)a.cnt_q)[row], a.by, a.Skv), 0};
   }
   auto fetch = [&](TileRef& r) -> bool {
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);

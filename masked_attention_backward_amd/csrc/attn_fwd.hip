@@ -68,7 +68,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     nt = max(0, ((hi + 63) >> 6) - tlo);
   } else {
     const size_t row = qhead * a.nqb + qb;
-    walk = TileWalker(a.sel_q + row * a.nkb, a.cnt_q[row], a.by, a.Skv);
+    walk = TileWalker(a.sel_q + row * a.nkb, ((const_int_ptr)a.cnt_q)[row], a.by, a.Skv);
   }
   int it = 0;
   auto next = [&](int& t, uint64_t& bits) -> bool {

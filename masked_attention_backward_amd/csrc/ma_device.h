@@ -98,15 +98,22 @@ __device__ __forceinline__ uint64_t range_bits(int a, int b) {
 // Walks the 64-row tiles covered by an ascending list of kept blocks (one row of a
 // selection table).  Each visited tile is reported once, in ascending order, with the
 // bitmask of its rows that lie inside a kept block and inside the sequence.
+// The list is read through the constant address space: the tables are written by an earlier
+// launch and only read here, and the walk is wave-uniform, so each entry is a scalar load
+// (scalar cache, counted by lgkmcnt) and never waits for the kernel's outstanding
+// global->LDS tile copies (vmcnt).
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
 struct TileWalker {
-  const int* sel;
+  const_int_ptr sel;
   int cnt, blk, len;
   int idx, last;
   __device__ TileWalker(const int* sel_, int cnt_, int blk_, int len_)
-      : sel(sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1) {}
+      : sel((const_int_ptr)sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1) {}
+  // Entry k of the list (wave-uniform k < cnt).
+  __device__ int entry(int k) const { return sel[k]; }
   __device__ bool next(int& tile, uint64_t& bits) {
     while (idx < cnt) {
-      const int j = sel[idx];
+      const int j = entry(idx);
       const int lo = j * blk;
       const int hi = min(lo + blk, len);
       int t = lo >> 6;
@@ -118,7 +125,7 @@ struct TileWalker {
       const int t0 = t * 64, t1 = t0 + 64;
       uint64_t m = 0;
       for (int k = idx; k < cnt; ++k) {
-        const int j2 = sel[k];
+        const int j2 = entry(k);
         const int lo2 = max(j2 * blk, t0);
         const int hi2 = min(min(j2 * blk + blk, len), t1);
         if (j2 * blk >= t1) break;
