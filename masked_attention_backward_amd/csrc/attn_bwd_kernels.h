@@ -388,8 +388,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     MA_STEP();
     // dS bank (window path): this wave's block, query block 2 tile + qh and key block
     // c0 / 32 + kb, is stored when it holds a visible pair (the bank's band), as this wave
-    // holds it: the two A operands of the dK product, each stored as soon as it is packed, so
-    // that the stores complete under this tile's remaining MFMAs (stores count in vmcnt, which
+    // holds it: the two A operands of the dK product, stored as soon as they are packed, so
+    // that the stores complete under this tile's dV/dK MFMAs (stores count in vmcnt, which
     // the next tile's first wait drains).  Non-temporal: the bank is read once, by the dQ
     // kernel, and should not displace the query tiles the other workgroups still read.
     bool ds_live = false;   // wave-uniform
@@ -402,7 +402,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
     }
     // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
-    // done one per MFMA between those eight MFMAs.
+    // done one per MFMA between those eight MFMAs (with a dS bank, all sixteen up front, so
+    // both bank stores go out before the dV/dK MFMAs and complete under them: the next tile's
+    // first wait covers stores as well as loads).
+    constexpr bool ROWS_UP_FRONT = MASK == MASK_WINDOW && DS;
     u32x4 pa[2], da[2];
     float pk = 0.f, dk2 = 0.f;
     auto srow = [&](auto rc) {
@@ -417,9 +420,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
         da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
       }
     };
-    static_for<0, 8>(srow);
-    if constexpr (MASK == MASK_WINDOW && DS) {
-      if (ds_live) __builtin_nontemporal_store(da[0], ds_dst);
+    static_for<0, ROWS_UP_FRONT ? 16 : 8>(srow);
+    if constexpr (ROWS_UP_FRONT) {
+      if (ds_live) {
+        __builtin_nontemporal_store(da[0], ds_dst);
+        __builtin_nontemporal_store(da[1], ds_dst + 64);
+      }
     }
     // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows.
     MA_STEP();
@@ -430,13 +436,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
         fc[(j + 1) & 1] = frag_col(stages, fo, 0, (j + 1) / 4, (j + 1) % 4);
       }
       dv[nb] = T::mma(pa[t], fb[j & 1], dv[nb]);
-      if constexpr (j < 4) srow(std::integral_constant<int, 8 + 2 * j>{});
+      if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 8 + 2 * j>{});
       MA_STEP();
       dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
-      if constexpr (j < 4) srow(std::integral_constant<int, 9 + 2 * j>{});
-      if constexpr (MASK == MASK_WINDOW && DS && j == 3) {
-        if (ds_live) __builtin_nontemporal_store(da[1], ds_dst + 64);
-      }
+      if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 9 + 2 * j>{});
       MA_STEP();
     });
     if (comp) {
