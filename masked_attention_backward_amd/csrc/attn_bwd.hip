@@ -154,13 +154,16 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   // window is wide the work per tile grows linearly along the sequence, so a workgroup
   // runs tile p and tile n-1-p (equal total work) whenever that still leaves at least
   // one workgroup per compute unit.
+  // dQ from a dS bank with a wide window: query tiles of 256 rows, eight waves sharing each
+  // staged key tile.
   const int nt = (a.Skv + 127) / 128;
   const bool wide = a.window >= 256 && a.window * 4 >= a.Skv;
-  const int pairs_dkdv = a.B * a.Hkv * ((nt + 1) / 2);
-  const int pairs_dq = a.B * a.Hq * ((nt + 1) / 2);
   AttnArgs ak = a, aq = a;
+  aq.dq_nw = (a.ds_bank && wide) ? 8 : 4;
   ak.n_tiles = nt;
-  aq.n_tiles = (a.Sq + 127) / 128;
+  aq.n_tiles = (a.Sq + 32 * aq.dq_nw - 1) / (32 * aq.dq_nw);
+  const int pairs_dkdv = a.B * a.Hkv * ((nt + 1) / 2);
+  const int pairs_dq = a.B * a.Hq * ((aq.n_tiles + 1) / 2);
   ak.pair = (wide && pairs_dkdv >= 256) ? 1 : 0;
   aq.pair = (wide && pairs_dq >= 256) ? 1 : 0;
   const int gk = a.B * a.Hkv * (ak.pair ? (ak.n_tiles + 1) / 2 : ak.n_tiles);

@@ -853,7 +853,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
 // 32 x 32 block, summed over the key blocks in ascending order (fixed, so results are
 // bit-identical run to run).  Workgroup = NW waves owning 32 NW consecutive query rows (wave w:
 // query block r0 / 32 + w).  Per 64-row key tile, one LDS stage holds the key tile and the two
-// dS blocks of every wave, all copied straight from HBM (LDS DMA), DQS_STAGES - 1 tiles ahead.
+// dS blocks of every wave, all copied straight from HBM (LDS DMA), one tile ahead with four
+// waves (two workgroups per compute unit) and two tiles ahead with eight (wide windows: one
+// workgroup of 256 query rows per compute unit, three stages, twice the bytes in flight per
+// compute unit and each key tile shared by twice the rows).
 // No softmax and no masking: masked entries of a stored block are exact zeros.
 //
 // A bank block holds dS as the dK/dV kernel's wave had it (lane 32 x + k: key k, slots s =
@@ -864,17 +867,17 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(const AttnArgs a) {
 // The copies place logical 16-byte chunk L = 32 x + 4 m + r (m = key / 4) of unit u at slot
 //   P = 16 (m / 2) + 8 (u ^ (m % 2)) + 4 x + r,
 // so that the 32 lanes of each half-wave read 32 distinct 8-byte bank pairs.
-constexpr int DQS_STAGES = 2;
-
 template <int NW>
 struct DqDsShape {
+  static constexpr int STAGES = NW == 8 ? 3 : 2;
   static constexpr int STAGE_B = TILE_BYTES + NW * 4096;   // key tile, then 2 dS blocks per wave
-  static constexpr int elems() { return DQS_STAGES * STAGE_B / 2; }
+  static constexpr int elems() { return STAGES * STAGE_B / 2; }
 };
 
 template <class T, int NW>
 __device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int r0, int q_end, uint16_t* smem) {
   using Sh = DqDsShape<NW>;
+  constexpr int DQS_STAGES = Sh::STAGES;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -1018,7 +1021,10 @@ template <class T, int MASK, int NW>
 inline void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
   if constexpr (MASK == MASK_WINDOW) {
     if (a.ds_bank) {
-      hipLaunchKernelGGL((dq_ds_kernel<T, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+      if (a.dq_nw == 8)
+        hipLaunchKernelGGL((dq_ds_kernel<T, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL((dq_ds_kernel<T, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
       return;
     }
   }

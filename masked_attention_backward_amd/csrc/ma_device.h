@@ -177,6 +177,7 @@ struct AttnArgs {
                          // read by the dQ GEMM (nullptr: dQ recomputes S and dP instead)
   int ds_kb;             // window path: ceil((window - 1) / 32), live key blocks below the diagonal
   long long ds_blocks;   // window path: live 32 x 32 blocks per (sequence, query head)
+  int dq_nw;             // window path with a dS bank: waves per dQ workgroup (4 or 8)
 };
 
 // Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per
