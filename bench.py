@@ -476,6 +476,8 @@ def main():
     ap.add_argument("--calls", type=int, default=4, help="calls per configuration per round")
     ap.add_argument("--dq-path", choices=["ds_bank", "recompute"], default="ds_bank",
                     help="sink path: workspace size selecting how dQ is computed")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample (about 2 s of back-to-back calls), e.g. under a profiler")
     ap.add_argument("--with-copy-probe", action="store_true",
                     help="also run one 256 MiB device-to-device copy (a kernel of known traffic, used to scale "
                          "hardware byte counters)")
@@ -569,7 +571,7 @@ def main():
             head.run()
         torch.cuda.synchronize()
 
-    clock = sample_clock_during(n_loop * ms_per_step / 1000.0 + 0.5, loop)
+    clock = None if args.no_clock else sample_clock_during(n_loop * ms_per_step / 1000.0 + 0.5, loop)
     rec["clock"] = clock
     clock_mhz = clock["mhz_median"] if clock else None
     if clock_mhz:

@@ -396,9 +396,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     u32x4* ds_dst = nullptr;
     if constexpr (MASK == MASK_WINDOW && DS) {
       const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
-      ds_live = kbk <= qa && kbk >= band_lo(qa, a.ds_kb) && qa * 32 < sq;
-      const long long blk =
-          ((long long)b * a.Hq + cur.head) * a.ds_blocks + band_offset(qa, a.ds_kb) + kbk - band_lo(qa, a.ds_kb);
+      ds_live = kbk <= qa && qa - a.ds_kb <= kbk && qa * 32 < sq;
+      // Entry within the head in 32-bit arithmetic (the launcher keeps a head's bank below
+      // 2^30 blocks), the head's base in 64-bit.
+      const int off = band_offset32(qa, a.ds_kb) + kbk - max(0, qa - a.ds_kb);
+      const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + off;
       ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
     }
     // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are

@@ -240,7 +240,8 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   a.window = window < S ? window : S;
   // A workspace large enough for the dS bank selects the dQ path that reads the dS blocks the
   // dK/dV kernel stores (one GEMM per block) instead of recomputing S and dP.
-  if (workspace_bytes >= attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, D, window)) {
+  if (workspace_bytes >= attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, D, window) &&
+      ds_blocks_of(S, window) < (1ll << 30)) {
     a.ds_bank = at<uint16_t>(workspace, need);
     a.ds_kb = (int)ds_kb_of(S, window);
     a.ds_blocks = ds_blocks_of(S, window);

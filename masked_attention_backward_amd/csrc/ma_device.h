@@ -213,5 +213,9 @@ __device__ __host__ __forceinline__ long long band_offset(long long a, long long
   // sum over a' < a of (min(a', kb) + 1)
   return a <= kb + 1 ? a * (a + 1) / 2 : (kb + 1) * (kb + 2) / 2 + (a - kb - 1) * (kb + 1);
 }
+// The same in 32-bit arithmetic, exact while the head's bank holds fewer than 2^30 blocks.
+__device__ __forceinline__ int band_offset32(int a, int kb) {
+  return a <= kb + 1 ? (a * (a + 1)) >> 1 : (((kb + 1) * (kb + 2)) >> 1) + (a - kb - 1) * (kb + 1);
+}
 
 }  // namespace ma
