@@ -145,6 +145,47 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// ------------------------------------------------------------------------ epilogue
+// Stores a wave's 32 x 128 tile of fp32 accumulators (accumulator nb: lane 32 h + c holds
+// column 32 nb + c of rows 8 (r / 4) + 4 h + r % 4) times `mul` to rows [0, nrows) of a
+// row-major 16-bit tensor at `dst` (row stride 128), in 16-byte pieces.  The values go through
+// a column-major LDS area of 128 columns x 36 elements (9216 B, 8-byte aligned, owned by the
+// wave): each lane writes its four consecutive rows of a column as 8 bytes, then one
+// ds_read_b64_tr_b16 gives each lane of a 16-lane group four consecutive columns of one row
+// (lane 4 r + a addresses rows 4 a .. 4 a + 3 of column C + r; lane j receives row j of
+// columns C .. C + 3), and two of them make the lane's 16 bytes.  Both passes touch 32
+// distinct 8-byte bank pairs per half-wave (the 72-byte column pitch).
+constexpr int EPI_PITCH = 36;                            // elements per staged column
+constexpr int EPI_ELEMS = 128 * EPI_PITCH;               // 4608 elements = 9216 B per wave
+
+template <class T>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[4], float mul, uint16_t* dst, int nrows,
+                                                uint16_t* stage, int lane) {
+  const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 v = {T::pack2s(acc[nb][4 * q4], acc[nb][4 * q4 + 1], mul),
+                       T::pack2s(acc[nb][4 * q4 + 2], acc[nb][4 * q4 + 3], mul)};
+      st8(stage + (32 * nb + c) * EPI_PITCH + 8 * q4 + 4 * h, v);
+    }
+  }
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  const int g = (lane >> 4) & 3, j = lane & 15, rr = j >> 2, aa = j & 3;
+  const int row = 16 * (g & 1) + j;                       // the row this lane stores
+  const uint16_t* rd = stage + rr * EPI_PITCH + 16 * (g & 1) + 4 * aa;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int col = 8 * (2 * s + (g >> 1));
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(rd + col * EPI_PITCH));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(rd + (col + 4) * EPI_PITCH));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    if (row < nrows) st16(dst + (size_t)row * HD + col, (u32x4){xa[0], xa[1], ya[0], ya[1]});
+  }
+}
+
 // ----------------------------------------------------------------------- dK / dV
 // Workgroup = 2 NK waves owning 32 NK consecutive key rows (NK = 4, 128 rows, on the window
 // path; NK = ceil(by / 32) on the block path, so a workgroup never straddles two key blocks).
@@ -555,25 +596,33 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       }
     }
   } else if (qh == 0) {
-    uint16_t* dKp = (uint16_t*)a.dk + kvrow0 * HD;
-    uint16_t* dVp = (uint16_t*)a.dv + kvrow0 * HD;
+    // Add the other half's partial sums (all of dK's first: the staging area below reuses the
+    // dK partials' LDS, which this wave alone reads), then store dK and dV in 16-byte pieces.
+    // LDS operations of one wave complete in order, so each staging write follows the reads
+    // of the partials it overwrites.
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 pk4 = red[(nb * 4 + q4) * 64];
-        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          const int row = c0 + 32 * kb + 8 * q4 + 4 * h + e;
-          if (row < kv_end) {
-            dKp[(size_t)row * HD + nb * 32 + c] = T::one((dk[nb][r] + pk4[e]) * a.scale);
-            dVp[(size_t)row * HD + nb * 32 + c] = T::one(dv[nb][r] + pv4[e]);
-          }
-        }
+        for (int e = 0; e < 4; ++e) dk[nb][4 * q4 + e] += pk4[e];
       }
     }
+    uint16_t* stage = smem + (size_t)kb * 32 * 64 * 8;   // this key block's exchange area
+    const size_t row0 = kvrow0 + c0 + 32 * kb;
+    const int nrows = kv_end - (c0 + 32 * kb);
+    store_tile_rows<T>(dk, a.scale, (uint16_t*)a.dk + row0 * HD, nrows, stage, lane);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[nb][4 * q4 + e] += pv4[e];
+      }
+    }
+    store_tile_rows<T>(dv, 1.f, (uint16_t*)a.dv + row0 * HD, nrows, stage, lane);
   }
 }
 
@@ -810,16 +859,11 @@ __device__ __forceinline__ void dq_tile(const AttnArgs& a, int b, int hq, int r0
   };
   while (vcur) vcur = step();
 
-  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
-  uint16_t* dQp = (uint16_t*)a.dq + qrow0 * HD;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
-    }
-  }
+  // Epilogue: rows r0 + 32 w .. of dQ, staged through this wave's part of the (now idle) K/V
+  // stages once every wave is done with them.
+  __syncthreads();
+  store_tile_rows<T>(acc, a.scale, (uint16_t*)a.dq + (qrow0 + r0 + 32 * w) * HD, q_end - (r0 + 32 * w),
+                     stages + w * EPI_ELEMS, lane);
 }
 
 template <class T, int MASK, int NW>
@@ -976,16 +1020,11 @@ __device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int
     s = s == DQS_STAGES - 1 ? 0 : s + 1;
   }
 
-  // Epilogue: rows r0 + 32w + 8(r/4) + 4h + r%4, column nb*32 + c.
-  uint16_t* dQp = (uint16_t*)a.dq + qrow0 * HD;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < q_end) dQp[(size_t)row * HD + nb * 32 + c] = T::one(acc[nb][r] * a.scale);
-    }
-  }
+  // Epilogue: rows r0 + 32 w .. of dQ, staged through this wave's part of the (now idle)
+  // stages once every wave is done with them.
+  __syncthreads();
+  store_tile_rows<T>(acc, a.scale, (uint16_t*)a.dq + (qrow0 + r0 + 32 * w) * HD, q_end - (r0 + 32 * w),
+                     smem + w * EPI_ELEMS, lane);
 }
 
 template <class T, int NW>

@@ -47,6 +47,13 @@ struct F16 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
   }
   static __device__ __forceinline__ uint16_t one(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  // Two products a s, b s rounded once each to half (mixed-precision FMA: the fp32 product is
+  // not rounded first).
+  static __device__ __forceinline__ uint32_t pack2s(float a, float b, float s) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(a * s));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(b * s));
+    return lo | (hi << 16);
+  }
 };
 
 struct BF16 {
@@ -61,6 +68,7 @@ struct BF16 {
   static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
   static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
   static __device__ __forceinline__ uint16_t one(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+  static __device__ __forceinline__ uint32_t pack2s(float a, float b, float s) { return pack2(a * s, b * s); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
