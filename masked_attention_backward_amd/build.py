@@ -24,8 +24,9 @@ INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [("capi.hip", "capi", []), ("attn_bwd.hip", "attn_bwd", []), ("attn_fwd.hip", "attn_fwd", []),
            ("mask_tables.hip", "mask_tables", [])]
 for _dt, _dtn in ((0, "f16"), (1, "bf16")):
-    SOURCES.append(("attn_bwd_variant.hip", f"bwd_{_dtn}_window_nw4",
-                    [f"-DMA_VARIANT_DTYPE={_dt}", "-DMA_VARIANT_MASK=0", "-DMA_VARIANT_NW=4"]))
+    for _nw in (2, 4):
+        SOURCES.append(("attn_bwd_variant.hip", f"bwd_{_dtn}_window_nw{_nw}",
+                        [f"-DMA_VARIANT_DTYPE={_dt}", "-DMA_VARIANT_MASK=0", f"-DMA_VARIANT_NW={_nw}"]))
     for _nw in (1, 2, 3, 4):
         SOURCES.append(("attn_bwd_variant.hip", f"bwd_{_dtn}_block_nw{_nw}",
                         [f"-DMA_VARIANT_DTYPE={_dt}", "-DMA_VARIANT_MASK=1", f"-DMA_VARIANT_NW={_nw}"]))

@@ -150,14 +150,16 @@ hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, in
 }
 
 hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid) {
-  // Key/value tiles of 128 rows (dK/dV) and query tiles of 128 rows (dQ).  When the
-  // window is wide the work per tile grows linearly along the sequence, so a workgroup
-  // runs tile p and tile n-1-p (equal total work) whenever that still leaves at least
-  // one workgroup per compute unit.
-  // dQ from a dS bank with a wide window: query tiles of 256 rows, eight waves sharing each
-  // staged key tile.
-  const int nt = (a.Skv + 127) / 128;
+  // Wide windows: key/value tiles of 128 rows (dK/dV, eight waves) and query tiles of 128
+  // rows (dQ).  The work per tile grows linearly along the sequence, so a workgroup runs tile
+  // p and tile n-1-p (equal total work) whenever that still leaves at least one workgroup per
+  // compute unit; dQ from a dS bank takes query tiles of 256 rows, eight waves sharing each
+  // staged key tile.  Narrow windows: dK/dV key tiles of 64 rows (four waves, one LDS stage,
+  // two workgroups per CU), whose query range [c0, c0 + 64 + W - 1) wastes less of each
+  // 64-row query tile on the band's edges than 128-row key tiles do.
   const bool wide = a.window >= 256 && a.window * 4 >= a.Skv;
+  const int bc = wide ? 128 : 64;
+  const int nt = (a.Skv + bc - 1) / bc;
   AttnArgs ak = a, aq = a;
   aq.dq_nw = (a.ds_bank && wide) ? 8 : 4;
   ak.n_tiles = nt;
@@ -168,8 +170,13 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   aq.pair = (wide && pairs_dq >= 256) ? 1 : 0;
   const int gk = a.B * a.Hkv * (ak.pair ? (ak.n_tiles + 1) / 2 : ak.n_tiles);
   const int gq = a.B * a.Hq * (aq.pair ? (aq.n_tiles + 1) / 2 : aq.n_tiles);
-  if (dtype == 1) launch_dkdv_variant<BF16, MASK_WINDOW, 4>(ak, gk, st);
-  else launch_dkdv_variant<F16, MASK_WINDOW, 4>(ak, gk, st);
+  if (wide) {
+    if (dtype == 1) launch_dkdv_variant<BF16, MASK_WINDOW, 4>(ak, gk, st);
+    else launch_dkdv_variant<F16, MASK_WINDOW, 4>(ak, gk, st);
+  } else {
+    if (dtype == 1) launch_dkdv_variant<BF16, MASK_WINDOW, 2>(ak, gk, st);
+    else launch_dkdv_variant<F16, MASK_WINDOW, 2>(ak, gk, st);
+  }
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   if (dtype == 1) launch_dq_variant<BF16, MASK_WINDOW, 4>(aq, gq, st);
   else launch_dq_variant<F16, MASK_WINDOW, 4>(aq, gq, st);

@@ -213,13 +213,13 @@ struct DkdvShape {
   static_assert(NK * 32 * 64 * 16 <= ROWS_OFF * 2, "partial-sum exchange must fit in the tile area");
 };
 
-// Stage count of the dK/dV pipeline.  Block path with key blocks of at most 64 rows: one
-// stage, so that two workgroups share a compute unit (two waves per SIMD; the loads of one
-// workgroup are hidden behind the other's matrix-core work, and so are the prologue and
-// epilogue of workgroups that walk only a few tiles).  Elsewhere two stages (the next tile's
-// loads are issued while the current one is computed).
+// Stage count of the dK/dV pipeline.  Key tiles of at most 64 rows (block path with small
+// key blocks; narrow windows): one stage, so that two workgroups share a compute unit (two
+// waves per SIMD; the loads of one workgroup are hidden behind the other's matrix-core work,
+// and so are the prologue and epilogue of workgroups that walk only a few tiles).  128-row
+// key tiles: two stages (the next tile's loads are issued while the current one is computed).
 template <int MASK, int NK>
-constexpr int dkdv_stages() { return (MASK == MASK_BLOCK && NK <= 2) ? 1 : 2; }
+constexpr int dkdv_stages() { return NK <= 2 ? 1 : 2; }
 // Waves per SIMD the dK/dV kernel's register budget is sized for (the second argument of
 // __launch_bounds__ on this target): two for the one-stage variant (at most 256 registers per
 // lane); the eight-wave workgroups of the other variants imply two by themselves.
