@@ -34,6 +34,17 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     len = min(s1 - s0, S);
   }
   const size_t phead = ((size_t)b * H + h) * (size_t)nblk * 64;
+  // All eight 16-byte loads of the thread go out before any is used (rows past the end read
+  // the last row, in bounds, and are not used): one memory round trip per workgroup.
+  u32x4 xs[4], ys[4];
+  if (len > 0) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rr = min(blk * 64 + pass * 16 + rsub, len - 1);
+      xs[pass] = ld16(o + (head + rr) * HD + ch * 8);
+      ys[pass] = ld16(dout + (head + rr) * HD + ch * 8);
+    }
+  }
   if (tid < 64) {
     const int row = blk * 64 + tid;
     // Rows past the end and rows that see no key at all (lse = -inf) get +inf: exp2(s - lse2)
@@ -46,8 +57,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     const int row = blk * 64 + pass * 16 + rsub;
     float acc = 0.f;
     if (row < len) {
-      const u32x4 x = ld16(o + (head + row) * HD + ch * 8);
-      const u32x4 y = ld16(dout + (head + row) * HD + ch * 8);
+      const u32x4 x = xs[pass], y = ys[pass];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc = fmaf(T::lo(x[e]), T::lo(y[e]), acc);
