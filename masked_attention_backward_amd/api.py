@@ -36,6 +36,7 @@ EXPORTS = (
     "attn_sink_bwd_varlen",
     "attn_sink_bwd_noalloc",
     "attn_sink_bwd_ds_workspace_bytes",
+    "blocksparse_attn_bwd_ds_workspace_bytes",
 )
 
 
@@ -83,6 +84,8 @@ def _load():
     lib.attn_sink_bwd_noalloc.restype = I
     lib.attn_sink_bwd_ds_workspace_bytes.argtypes = [I] * 6
     lib.attn_sink_bwd_ds_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_ds_workspace_bytes.argtypes = [I] * 7
+    lib.blocksparse_attn_bwd_ds_workspace_bytes.restype = Z
     return lib
 
 
@@ -298,6 +301,10 @@ def blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D=128):
     return int(lib.blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, D, bx, by))
 
 
+def blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, bx, by, D=128):
+    return int(lib.blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, D, bx, by))
+
+
 def _block_shapes(q, k, block_mask, bx, by):
     B, N, Sq, D = q.shape
     Nkv, Skv = k.shape[1], k.shape[2]
@@ -330,7 +337,11 @@ def blocksparse_attn_fwd(q, k, v, block_mask, bx, by, scale=None, workspace=None
 
 
 def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, workspace=None):
-    """Block-sparse backward -> (dq, dk, dv); k/v (and dk/dv) may have fewer heads (GQA)."""
+    """Block-sparse backward -> (dq, dk, dv); k/v (and dk/dv) may have fewer heads (GQA).
+
+    Without a workspace one of blocksparse_attn_bwd_ds_workspace_bytes() is allocated (the
+    dS-bank path when bx and by are multiples of 32); a caller workspace of
+    blocksparse_attn_bwd_workspace_bytes() selects the recompute path."""
     B, N, Nkv, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
     dev = q.device
     for name, t in (("q", q), ("o", o), ("do", do)):
@@ -339,7 +350,8 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     _need(v, "v", (B, Nkv, Skv, D), q.dtype, dev)
     _need(lse, "lse", (B, N, Sq), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev, workspace)
+    ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev, workspace) \
+        if workspace is not None else _workspace(blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

@@ -434,7 +434,18 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // the next tile's first wait drains).  Non-temporal: the bank is read once, by the dQ
     // kernel, and should not displace the query tiles the other workgroups still read.
     bool ds_live = false;   // wave-uniform
+    bool ds_edge = false;   // wave-uniform: the block reaches past the last key row
     u32x4* ds_dst = nullptr;
+    if constexpr (MASK == MASK_BLOCK && DS) {
+      // Block path (block sizes multiples of 32, so this wave's 32 x 32 block lies inside one
+      // mask block): entry (head, qa, ka) of the dense grid, stored when some of its query
+      // rows are selected; key columns past the last key row are stored as zeros.
+      const int qa = 2 * cur.tile + qh, ka = (c0 >> 5) + kb;
+      ds_live = ((cur.bits >> (32 * qh)) & 0xffffffffull) != 0 && ka * 32 < kv_end;
+      ds_edge = ka * 32 + 32 > kv_end;
+      const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + (qa * a.ds_nka + ka);
+      ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
+    }
     if constexpr (MASK == MASK_WINDOW && DS) {
       const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
       ds_live = kbk <= qa && qa - a.ds_kb <= kbk && qa * 32 < sq;
@@ -448,7 +459,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // done one per MFMA between those eight MFMAs (with a dS bank, all sixteen up front, so
     // both bank stores go out before the dV/dK MFMAs and complete under them: the next tile's
     // first wait covers stores as well as loads).
-    constexpr bool ROWS_UP_FRONT = MASK == MASK_WINDOW && DS;
+    constexpr bool ROWS_UP_FRONT = DS;
     u32x4 pa[2], da[2];
     float pk = 0.f, dk2 = 0.f;
     auto srow = [&](auto rc) {
@@ -465,6 +476,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     };
     static_for<0, ROWS_UP_FRONT ? 16 : 8>(srow);
     if constexpr (ROWS_UP_FRONT) {
+      if (MASK == MASK_BLOCK && ds_edge && kj >= kv_end) {
+        // Key rows past the end: dS of these columns is garbage computed on clamped K rows;
+        // zero it (it only feeds dK rows that are never stored, and the dQ product).
+        da[0] = (u32x4){0u, 0u, 0u, 0u};
+        da[1] = (u32x4){0u, 0u, 0u, 0u};
+      }
       if (ds_live) {
         __builtin_nontemporal_store(da[0], ds_dst);
         __builtin_nontemporal_store(da[1], ds_dst + 64);
@@ -654,7 +671,7 @@ __global__ __launch_bounds__(2 * NK * 64, (dkdv_waves_per_simd<MASK, NK>())) voi
     const int nch = block_chunks(a, b, kvh, kblock);
     if (chunk >= nch) return;   // uniform: no loads or barriers issued yet
     const int c0 = kblock * a.by;
-    dkdv_tile<T, MASK, NK>(a, b, kvh, c0, min(c0 + a.by, a.Skv), kblock, smem, chunk, nch > 1);
+    dkdv_tile<T, MASK, NK, DS>(a, b, kvh, c0, min(c0 + a.by, a.Skv), kblock, smem, chunk, nch > 1);
   }
 }
 
@@ -1045,15 +1062,113 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_ds_kernel(const AttnArgs a) {
   }
 }
 
+// Block path with a dS bank (block sizes multiples of 32): dQ of query block qb (bx rows; NW =
+// bx / 32 waves, wave w owning the 32-row query block qa = qb bx / 32 + w) from the bank.  The
+// key tiles come from the query block's row of the q-major table (ascending, so the sum over
+// key blocks has a fixed order); a selected mask block covers whole 32-row key blocks, so each
+// 64-row tile's two 32-row halves are either selected (one GEMM each, dS copied from the bank)
+// or skipped.  Stages as in dq_ds_tile (key tile + two dS blocks per wave, transposing reads).
+template <class T, int NW>
+__device__ __forceinline__ void dq_ds_block_tile(const AttnArgs& a, int b, int hq, int qb, uint16_t* smem) {
+  constexpr int STAGE_B = TILE_BYTES + NW * 4096;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  const int r0 = qb * a.bx, q_end = min(r0 + a.bx, sq);
+  const size_t qrow0 = qs.base + (size_t)hq * qs.head_stride;
+  const int kvh = hq / a.group;
+  const uint16_t* Kp = (const uint16_t*)a.k + (ks.base + (size_t)kvh * ks.head_stride) * HD;
+  const int qa = (r0 >> 5) + wu;
+  const bool rows = qa * 32 < q_end;
+  const uint16_t* bank =
+      a.ds_bank + (((long long)b * a.Hq + hq) * a.ds_blocks + (long long)(rows ? qa : 0) * a.ds_nka) * 1024;
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  TileWalker walk(a.sel_q + (qhead * a.nqb + qb) * a.nkb, a.cnt_q[qhead * a.nqb + qb], a.by, a.Skv);
+
+  auto src_chunk = [&](int u) -> uint32_t {
+    const int m = 2 * (lane >> 4) + (((lane >> 3) & 1) ^ u);
+    return (uint32_t)(u * 1024 + (32 * ((lane >> 2) & 1) + 4 * m + (lane & 3)) * 16);
+  };
+  const uint32_t so0 = src_chunk(0), so1 = src_chunk(1);
+  const int g = (lane >> 4) & 1, ia = lane & 3, ir = (lane >> 2) & 3;
+  const int dso = g * 1024 + 128 * (g ^ h) + 64 * (ia & 1) + 16 * ir + 8 * (ia >> 1);
+  auto half_live = [](uint64_t bits, int mb) { return ((bits >> (32 * mb)) & 0xffffffffull) != 0; };
+  auto issue = [&](const TileRef& r, int s) {
+    const uint32_t st = smem_lds + (uint32_t)(s * STAGE_B);
+    tile_load_async<NW>(st, Kp, r.tile * 64, skv, wu, lane);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (rows && half_live(r.bits, mb)) {
+        const uint16_t* blk = bank + (long long)(2 * r.tile + mb) * 1024;
+        const uint32_t d = st + (uint32_t)(TILE_BYTES + wu * 4096 + mb * 2048);
+        dma16(blk, so0, __builtin_amdgcn_readfirstlane(d));
+        dma16(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+      }
+    }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+  FragOff fo(lane);
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  auto ds_frag = [&](const char* blk, int tt) -> u32x4 {
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt + 256));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    return (u32x4){xa[0], xa[1], ya[0], ya[1]};
+  };
+
+  TileRef cur{}, nx{};
+  bool vcur = walk.next(cur.tile, cur.bits);
+  if (vcur) issue(cur, 0);
+  int s = 0;
+  while (vcur) {
+    wait_vmcnt<0>();   // this tile's copies (the next tile's go out after the barrier)
+    __syncthreads();
+    const bool vn = walk.next(nx.tile, nx.bits);
+    if (vn) issue(nx, s ^ 1);
+    const uint16_t* kt = smem + s * (STAGE_B / 2);
+    const char* dsb = reinterpret_cast<const char*>(smem) + s * STAGE_B + TILE_BYTES + wu * 4096;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (rows && half_live(cur.bits, mb)) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const u32x4 fa = ds_frag(dsb + mb * 2048, tt);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa, frag_col(kt, fo, 0, 2 * mb + tt, nb), acc[nb]);
+        }
+      }
+    }
+    s ^= 1;
+    cur = nx;
+    vcur = vn;
+  }
+  __syncthreads();
+  store_tile_rows<T>(acc, a.scale, (uint16_t*)a.dq + (qrow0 + r0 + 32 * w) * HD, q_end - (r0 + 32 * w),
+                     smem + w * EPI_ELEMS, lane);
+}
+
+template <class T, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void dq_ds_block_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (TILE_BYTES + NW * 4096) / 2];
+  const int nbh = a.B * a.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % nbh, qb = wg / nbh;
+  dq_ds_block_tile<T, NW>(a, bh / a.Hq, bh % a.Hq, qb, smem);
+}
+
 // Launch of one (element type, mask kind, NW) variant: dK/dV with 2 NW waves (NW key blocks
 // of 32 rows), dQ with NW waves (NW query blocks of 32 rows).
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
-  if constexpr (MASK == MASK_WINDOW) {
-    if (a.ds_bank) {
-      hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW, true>), dim3(grid), dim3(2 * NW * 64), 0, st, a);
-      return;
-    }
+  if (a.ds_bank) {
+    hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW, true>), dim3(grid), dim3(2 * NW * 64), 0, st, a);
+    return;
   }
   hipLaunchKernelGGL((dkdv_kernel<T, MASK, NW>), dim3(grid), dim3(2 * NW * 64), 0, st, a);
 }
@@ -1066,6 +1181,11 @@ inline void launch_dq_only(const AttnArgs& a, int grid, hipStream_t st) {
         hipLaunchKernelGGL((dq_ds_kernel<T, 8>), dim3(grid), dim3(8 * 64), 0, st, a);
       else
         hipLaunchKernelGGL((dq_ds_kernel<T, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
+      return;
+    }
+  } else {
+    if (a.ds_bank) {
+      hipLaunchKernelGGL((dq_ds_block_kernel<T, NW>), dim3(grid), dim3(NW * 64), 0, st, a);
       return;
     }
   }

@@ -186,6 +186,8 @@ struct AttnArgs {
   int ds_kb;             // window path: ceil((window - 1) / 32), live key blocks below the diagonal
   long long ds_blocks;   // window path: live 32 x 32 blocks per (sequence, query head)
   int dq_nw;             // window path with a dS bank: waves per dQ workgroup (4 or 8)
+  int ds_nka;            // block path with a dS bank: 32-row key blocks per 32-row query block
+                         // (bank entry of (head, qa, ka): head * ds_blocks + qa * ds_nka + ka)
 };
 
 // Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per

@@ -125,6 +125,30 @@ def test_ds_workspace_query(lib):
     assert lib.attn_sink_bwd_ds_workspace_bytes(1, 4, 1, 128, 64, 10) == 0
 
 
+def test_block_ds_workspace_query(lib):
+    """The block path's dS-bank workspace: the minimum one plus 2048 bytes per cell of the
+    dense grid of 32 x 32 blocks of every (batch, query head) when bx and by are multiples of
+    32; the minimum one otherwise (no bank: the tilings of the two kernels differ)."""
+    Z, I = ctypes.c_size_t, ctypes.c_int
+    lib.blocksparse_attn_bwd_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_workspace_bytes.argtypes = [I] * 7
+    lib.blocksparse_attn_bwd_ds_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_ds_workspace_bytes.argtypes = [I] * 7
+    for B, N, Sq, Skv, bx, by in [(1, 16, 8192, 8192, 64, 64), (2, 3, 200, 190, 32, 96), (1, 2, 1, 1, 128, 32),
+                                  (2, 8, 3000, 3000, 48, 80), (1, 4, 300, 500, 64, 16), (1, 1, 77, 65, 96, 128)]:
+        base = lib.blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, 128, bx, by)
+        full = lib.blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, 128, bx, by)
+        assert base > 0
+        if bx % 32 == 0 and by % 32 == 0:
+            bank = B * N * (-(-Sq // 32)) * (-(-Skv // 32)) * 2048
+            assert full == base + (bank + 255) // 256 * 256, (B, N, Sq, Skv, bx, by)
+        else:
+            assert full == base, (bx, by)
+    assert lib.blocksparse_attn_bwd_ds_workspace_bytes(1, 16, 8192, 8192, 128, 64, 64) == \
+        lib.blocksparse_attn_bwd_workspace_bytes(1, 16, 8192, 8192, 128, 64, 64) + 16 * 256 * 256 * 2048
+    assert lib.blocksparse_attn_bwd_ds_workspace_bytes(1, 4, 128, 128, 64, 64, 64) == 0   # D = 64
+
+
 def test_blocksparse_validation(lib):
     V, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     f = lib.blocksparse_attn_bwd

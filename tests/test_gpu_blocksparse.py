@@ -26,14 +26,25 @@ def with_oracle_forward(wl, x):
     return x
 
 
-def gpu_bwd(wl, x):
+def gpu_bwd(wl, x, path="default"):
+    """path "default": the binding's workspace (the dS bank when bx and by are multiples of 32);
+    "recompute": the minimum workspace (dQ recomputes S and dP)."""
     g = {k: v.to(DEV) for k, v in x.items()}
-    print(f"[gpu] blocksparse_attn_bwd {wl.name} B{wl.B} N{wl.Hq} Sq{wl.Sq} Skv{wl.Skv} bx{wl.bx} by{wl.by}",
+    print(f"[gpu] blocksparse_attn_bwd {wl.name} B{wl.B} N{wl.Hq} Sq{wl.Sq} Skv{wl.Skv} bx{wl.bx} by{wl.by} {path}",
           flush=True)
+    ws = None
+    if path == "recompute":
+        a = api()
+        ws = torch.empty(a.blocksparse_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv, wl.bx, wl.by),
+                         dtype=torch.uint8, device=DEV)
     out = api().blocksparse_attn_bwd(g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["block_mask"], wl.bx,
-                                     wl.by, wl.scale)
+                                     wl.by, wl.scale, workspace=ws)
     torch.cuda.synchronize()
     return out
+
+
+def banked(wl):
+    return wl.bx % 32 == 0 and wl.by % 32 == 0
 
 
 @pytest.mark.parametrize("name", ["bigbird", "ragged"])
@@ -87,10 +98,14 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
-def test_bwd_small(wl):
+# Block sizes that are multiples of 32 run both dQ paths (dS bank, recompute); others have one.
+SMALL_PATHS = [(wl, p) for wl in SMALL for p in (("default", "recompute") if banked(wl) else ("default",))]
+
+
+@pytest.mark.parametrize("wl,path", SMALL_PATHS, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_bwd_small(wl, path):
     x = with_oracle_forward(wl, W.make_inputs(wl))
-    dq, dk, dv = gpu_bwd(wl, x)
+    dq, dk, dv = gpu_bwd(wl, x, path)
     ref = oracle.blocksparse_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["block_mask"],
                                                 wl.bx, wl.by, wl.scale)
     check("dq", dq, ref["dq"], wl.dtype)
