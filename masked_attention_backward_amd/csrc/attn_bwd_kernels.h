@@ -280,17 +280,58 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);
     else return bsrc.next(r.head, r.tile, r.bits);
   };
-  StageLoads<NWV> nx;
-  auto issue = [&](const TileRef& r, int stg) {
-    const size_t qhead = (size_t)b * a.Hq + r.head;
-    const size_t qrow0 = qs.base + (size_t)r.head * qs.head_stride;
-    nx.prepare((const uint16_t*)a.q + qrow0 * HD, (const uint16_t*)a.dout + qrow0 * HD,
-               stages_lds + (uint32_t)(stg * STAGE_BYTES), r.tile * 64, sq, wu, lane);
+  // Copies of a visited tile: the lane offsets inside a 64-row tile are fixed (computed once;
+  // the swizzle is applied on the global side); a visit only moves the wave-uniform bases to
+  // its head and tile, and only a tile reaching past the sequence end clamps its rows.
+  constexpr int J = StageLoads<NWV>::J;
+  const int head0 = kvh * a.group;   // every visited head is head0 + (0 .. group - 1)
+  const uint16_t* q0 = (const uint16_t*)a.q + (qs.base + (size_t)head0 * qs.head_stride) * HD;
+  const uint16_t* o0 = (const uint16_t*)a.dout + (qs.base + (size_t)head0 * qs.head_stride) * HD;
+  const size_t hstride = qs.head_stride * HD;
+  const float* l0 = a.lse2 + ((size_t)b * a.Hq + head0) * sq_pad;
+  const float* d0 = a.delta + ((size_t)b * a.Hq + head0) * sq_pad;
+  uint32_t voff[J];
 #pragma unroll
-    for (int i = 0; i < 2 * StageLoads<NWV>::J; ++i) nx.issue(i, wu);
+  for (int j = 0; j < J; ++j) {
+    const int row = 4 * (wu + j * NWV) + (lane >> 4);
+    voff[j] = 2u * (uint32_t)(row * HD + (((lane & 15) ^ swz(row)) << 3));
+  }
+  auto issue = [&](const TileRef& r, int stg) {
+    const int dh = r.head - head0;
+    const size_t off = (size_t)dh * hstride + (size_t)r.tile * (64 * HD);
+    const uint16_t* qb = q0 + off;
+    const uint16_t* ob = o0 + off;
+    const uint32_t dst = stages_lds + (uint32_t)(stg * STAGE_BYTES);
+    if (r.tile * 64 + 64 <= sq) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (StageLoads<NWV>::exists(j, wu))
+          dma16(qb, voff[j], __builtin_amdgcn_readfirstlane(dst + (uint32_t)((wu + j * NWV) * 1024)));
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (StageLoads<NWV>::exists(j, wu))
+          dma16(ob, voff[j], __builtin_amdgcn_readfirstlane(dst + (uint32_t)(TILE_BYTES + (wu + j * NWV) * 1024)));
+    } else {
+      const int last = sq - 1 - r.tile * 64;   // last row of the tile inside the sequence
+      uint32_t cl[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int row = 4 * (wu + j * NWV) + (lane >> 4);
+        cl[j] = 2u * (uint32_t)(min(row, last) * HD + (((lane & 15) ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (StageLoads<NWV>::exists(j, wu))
+          dma16(qb, cl[j], __builtin_amdgcn_readfirstlane(dst + (uint32_t)((wu + j * NWV) * 1024)));
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (StageLoads<NWV>::exists(j, wu))
+          dma16(ob, cl[j], __builtin_amdgcn_readfirstlane(dst + (uint32_t)(TILE_BYTES + (wu + j * NWV) * 1024)));
+    }
     const uint32_t rows = sld_lds + (uint32_t)(stg * 512);
-    if (wu == 0) row_load_async(rows, a.lse2 + qhead * sq_pad + r.tile * 64, lane);
-    if (wu == NWV - 1) row_load_async(rows + 256, a.delta + qhead * sq_pad + r.tile * 64, lane);
+    const size_t roff = (size_t)dh * sq_pad + r.tile * 64;
+    if (wu == 0) row_load_async(rows, l0 + roff, lane);
+    if (wu == NWV - 1) row_load_async(rows + 256, d0 + roff, lane);
   };
 
   // V is negated in LDS once it has landed (sign bit of every 16-bit element), right after
