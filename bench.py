@@ -53,8 +53,9 @@ KERNEL_SOURCES = ["attn_bwd_kernels.h", "attn_bwd.hip", "attn_bwd_variant.hip", 
 BOUND = {"tiny": "launch", "mid": "hbm", "large_w128": "hbm", "large_causal": "mfma", "bigbird": "hbm",
          "ragged": "mfma", "pages_h64_s4096": "mfma", "pages_h64_s4096_fwd": "mfma", "varlen_8x2048": "mfma",
          "varlen_mixed": "mfma"}
-# Sink path: workspace size that selects the dQ path ("ds_bank": the dK/dV kernel stores dS and
-# dQ is one GEMM per block; "recompute": the minimum workspace, dQ recomputes S and dP).
+# Workspace size that selects the dQ path ("ds_bank": the dK/dV kernel stores dS and dQ is one
+# GEMM per block -- on the block path only when bx and by are multiples of 32, the library
+# recomputing otherwise; "recompute": the minimum workspace, dQ recomputes S and dP).
 DQ_PATH = "ds_bank"
 CONFIG_ORDER = ["tiny", "mid", "large_w128", "large_causal", "bigbird", "ragged", "pages_h64_s4096",
                 "pages_h64_s4096_fwd", "varlen_8x2048", "varlen_mixed"]
@@ -309,6 +310,15 @@ class Case:
         self.flops, self.alg_bytes, self.dtype, self.config = flops, alg_bytes, dtype, config
 
 
+def dq_path_of(case):
+    """The dQ path a backward case runs (None for the forward)."""
+    if case.kind in ("sink", "varlen"):
+        return DQ_PATH
+    if case.kind == "blocksparse":
+        return DQ_PATH if case.wl.bx % 32 == 0 and case.wl.by % 32 == 0 else "recompute"
+    return None
+
+
 def make_case(name, dev):
     import torch
     from masked_attention_backward_amd import api, workloads as W
@@ -374,7 +384,9 @@ def make_case(name, dev):
                   else api.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq))
     else:
         o, lse = api.blocksparse_attn_fwd(g["q"], g["k"], g["v"], g["block_mask"], wl.bx, wl.by, wl.scale)
-        nbytes = api.blocksparse_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv, wl.bx, wl.by)
+        nbytes = (api.blocksparse_attn_bwd_ds_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv, wl.bx, wl.by)
+                  if DQ_PATH == "ds_bank" else api.blocksparse_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.Skv,
+                                                                                       wl.bx, wl.by))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
     dsink = torch.empty(wl.Hq, dtype=torch.float32, device=dev)
@@ -456,7 +468,8 @@ def config_record(case, times, warm_ms, clock_mhz, oracle):
            "pct_peak_mfma_at_clock": round(100 * tflops / peak_clk, 2) if peak_clk else None,
            "algorithmic_bytes": case.alg_bytes, "hbm_gbs_algorithmic": round(gbs, 1),
            "pct_hbm_8tbs": round(100 * gbs / PEAK_HBM, 2), "bound": bound,
-           "frac_of_bound": round(tflops / PEAK_MFMA_16BIT if bound == "mfma" else gbs / PEAK_HBM, 4)}
+           "frac_of_bound": round(tflops / PEAK_MFMA_16BIT if bound == "mfma" else gbs / PEAK_HBM, 4),
+           "dq_path": dq_path_of(case)}
     if oracle is not None:
         rec["oracle"] = oracle
     return rec
@@ -475,7 +488,7 @@ def main():
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--calls", type=int, default=4, help="calls per configuration per round")
     ap.add_argument("--dq-path", choices=["ds_bank", "recompute"], default="ds_bank",
-                    help="sink path: workspace size selecting how dQ is computed")
+                    help="workspace size selecting how dQ is computed")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the shader-clock sample (about 2 s of back-to-back calls), e.g. under a profiler")
     ap.add_argument("--with-copy-probe", action="store_true",
@@ -534,7 +547,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": head.dtype,
         "data": "synthetic (seeded N(0,1) inputs; O, lse from the library forward)",
-        "config": head.config, "dq_path": DQ_PATH if head.kind in ("sink", "varlen") else None,
+        "config": head.config, "dq_path": dq_path_of(head),
         "pct_peak_mfma": round(100.0 * tflops / PEAK_MFMA_16BIT, 2),
         "counted_tflop": round(head.flops / 1e12, 4),
     }

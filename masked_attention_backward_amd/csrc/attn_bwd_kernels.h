@@ -1023,8 +1023,13 @@ __device__ __forceinline__ void dq_ds_tile(const AttnArgs& a, int b, int hq, int
       const int kb = rows ? min(max(2 * t + mb, mlo), mhi) : 0;
       const uint16_t* blk = bank + (long long)kb * 1024;
       const uint32_t d = st + (uint32_t)(TILE_BYTES + wu * 4096 + mb * 2048);
-      dma16(blk, so0, __builtin_amdgcn_readfirstlane(d));
-      dma16(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+      if constexpr (NW == 8) {   // bank blocks are read once (measured faster with three stages)
+        dma16nt(blk, so0, __builtin_amdgcn_readfirstlane(d));
+        dma16nt(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+      } else {
+        dma16(blk, so0, __builtin_amdgcn_readfirstlane(d));
+        dma16(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+      }
     }
   };
 

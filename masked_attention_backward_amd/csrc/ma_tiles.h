@@ -104,6 +104,11 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "m0");
 }
+// The same with the non-temporal hint (data read once: streamed through L2 rather than kept).
+__device__ __forceinline__ void dma16nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "m0");
