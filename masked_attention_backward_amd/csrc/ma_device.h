@@ -120,6 +120,25 @@ struct TileWalker {
   // Entry k of the list (wave-uniform k < cnt).
   __device__ int entry(int k) const { return sel[k]; }
   __device__ bool next(int& tile, uint64_t& bits) {
+    if ((blk & 63) == 0) {
+      // Blocks of whole 64-row tiles: a tile lies in one block, its bits are that block's rows
+      // (all of them but in the sequence's last tile), and one entry load serves the tile.
+      while (idx < cnt) {
+        const int j = entry(idx);
+        const int hi = min(j * blk + blk, len);
+        const int t = max(j * (blk >> 6), last + 1);
+        if (t * 64 >= hi) {
+          ++idx;
+          continue;
+        }
+        if (t * 64 + 64 >= hi) ++idx;   // the block's last tile
+        last = t;
+        tile = t;
+        bits = range_bits(0, hi - t * 64);
+        return true;
+      }
+      return false;
+    }
     while (idx < cnt) {
       const int j = entry(idx);
       const int lo = j * blk;
