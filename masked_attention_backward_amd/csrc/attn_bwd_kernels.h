@@ -385,6 +385,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       __syncthreads();
     }
     const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
+    // The next tile.  One stage: found before this tile's LDS reads are issued (a table entry
+    // read on the block path is a scalar load, whose wait would otherwise cover those reads as
+    // well); two stages: found, and its loads issued, once the first reads are in flight.
+    TileRef nxr{};
+    bool vn = false;
+    if constexpr (NSTAGE == 1) vn = fetch(nxr);
 
     // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
     typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
@@ -405,9 +411,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     fk[0] = frag_row(kvs, fkv, 0, 0, 0);
     fd[0] = frag_row(stages, fo, 1, 0, 0);
     fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
-    TileRef nxr{};
-    const bool vn = fetch(nxr);
     if constexpr (NSTAGE == 2) {
+      vn = fetch(nxr);
       if (vn) issue(nxr, stg ^ 1);
     }
     MA_STEP();

@@ -115,23 +115,31 @@ struct TileWalker {
   const_int_ptr sel;
   int cnt, blk, len;
   int idx, last;
+  int pj;   // whole-tile walk: entry(idx), loaded by the previous call (pj < 0: not loaded)
   __device__ TileWalker(const int* sel_, int cnt_, int blk_, int len_)
-      : sel((const_int_ptr)sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1) {}
+      : sel((const_int_ptr)sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1), pj(-1) {}
   // Entry k of the list (wave-uniform k < cnt).
   __device__ int entry(int k) const { return sel[k]; }
   __device__ bool next(int& tile, uint64_t& bits) {
     if ((blk & 63) == 0) {
       // Blocks of whole 64-row tiles: a tile lies in one block, its bits are that block's rows
-      // (all of them but in the sequence's last tile), and one entry load serves the tile.
+      // (all of them but in the sequence's last tile), and one entry load serves the tile; it
+      // is issued one call ahead, so the caller does not wait for it.
       while (idx < cnt) {
-        const int j = entry(idx);
+        const int j = pj >= 0 ? pj : entry(idx);
+        pj = -1;
         const int hi = min(j * blk + blk, len);
         const int t = max(j * (blk >> 6), last + 1);
         if (t * 64 >= hi) {
           ++idx;
           continue;
         }
-        if (t * 64 + 64 >= hi) ++idx;   // the block's last tile
+        if (t * 64 + 64 >= hi) {   // the block's last tile
+          ++idx;
+          if (idx < cnt) pj = entry(idx);
+        } else {
+          pj = j;
+        }
         last = t;
         tile = t;
         bits = range_bits(0, hi - t * 64);
