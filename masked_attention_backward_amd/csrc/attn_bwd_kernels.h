@@ -621,71 +621,56 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   wait_vmcnt<0>();   // K/V loads when there was no tile at all
   __syncthreads();
 
-  // Partial sums of waves w + NK into LDS (16-byte chunks, lane-major), added by waves w.
+  // Waves w + NK hand their partial dK sums to waves w, which hand their partial dV sums back
+  // (16-byte chunks, lane-major; key block kb's 32 KiB area holds dK's at its start and dV's
+  // at +16 KiB); then waves w store dK and waves w + NK store dV, each adding the other half's
+  // sums to its own (floating-point addition commutes: the bits do not depend on who adds).
   f32x4* red = reinterpret_cast<f32x4*>(smem) + (size_t)kb * 32 * 64 + lane;
-  if (qh == 1) {
+  f32x4* mine = red + (qh == 0 ? 16 * 64 : 0);    // where this wave's partials go
+  f32x4* theirs = red + (qh == 0 ? 0 : 16 * 64);  // where the other half's arrive
+  f32x16 (&keep)[4] = qh == 0 ? dk : dv;           // the sums this wave stores
+  {
+    const f32x16 (&give)[4] = qh == 0 ? dv : dk;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        red[(nb * 4 + q4) * 64] = (f32x4){dk[nb][4 * q4], dk[nb][4 * q4 + 1], dk[nb][4 * q4 + 2], dk[nb][4 * q4 + 3]};
-        red[(16 + nb * 4 + q4) * 64] = (f32x4){dv[nb][4 * q4], dv[nb][4 * q4 + 1], dv[nb][4 * q4 + 2], dv[nb][4 * q4 + 3]};
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        mine[(nb * 4 + q4) * 64] =
+            (f32x4){give[nb][4 * q4], give[nb][4 * q4 + 1], give[nb][4 * q4 + 2], give[nb][4 * q4 + 3]};
     }
   }
   __syncthreads();
-  if (qh == 0 && partial) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 o4 = theirs[(nb * 4 + q4) * 64];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[nb][4 * q4 + e] += o4[e];
+    }
+  }
+  const float mul = qh == 0 ? a.scale : 1.f;
+  if (partial) {
     // One chunk of a key block whose selected query blocks span several workgroups: fp32
     // partial sums, added in chunk order and cast by the dK/dV reduce kernel.
     const int skv_pad = (a.Skv + 63) & ~63;
     const size_t slab = (size_t)a.B * a.Hkv * a.max_chunks * skv_pad * HD;
-    float* pk = a.dkv_part + (((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk) * skv_pad * HD;
-    float* pv = pk + slab;
+    float* pk = a.dkv_part + (((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk) * skv_pad * HD + (qh ? slab : 0);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 pk4 = red[(nb * 4 + q4) * 64];
-        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          const int row = c0 + 32 * kb + 8 * q4 + 4 * h + e;
-          if (row < kv_end) {
-            pk[(size_t)row * HD + nb * 32 + c] = (dk[nb][r] + pk4[e]) * a.scale;
-            pv[(size_t)row * HD + nb * 32 + c] = dv[nb][r] + pv4[e];
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = c0 + 32 * kb + 8 * (r / 4) + 4 * h + r % 4;
+        if (row < kv_end) pk[(size_t)row * HD + nb * 32 + c] = keep[nb][r] * mul;
       }
     }
-  } else if (qh == 0) {
-    // Add the other half's partial sums (all of dK's first: the staging area below reuses the
-    // dK partials' LDS, which this wave alone reads), then store dK and dV in 16-byte pieces.
-    // LDS operations of one wave complete in order, so each staging write follows the reads
-    // of the partials it overwrites.
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 pk4 = red[(nb * 4 + q4) * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dk[nb][4 * q4 + e] += pk4[e];
-      }
-    }
-    uint16_t* stage = smem + (size_t)kb * 32 * 64 * 8;   // this key block's exchange area
+  } else {
+    // 16-byte stores through the area the partials arrived in (this wave alone read it; LDS
+    // operations of one wave complete in order, so each staging write follows those reads).
+    uint16_t* stage = reinterpret_cast<uint16_t*>(theirs - lane);
     const size_t row0 = kvrow0 + c0 + 32 * kb;
     const int nrows = kv_end - (c0 + 32 * kb);
-    store_tile_rows<T>(dk, a.scale, (uint16_t*)a.dk + row0 * HD, nrows, stage, lane);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 pv4 = red[(16 + nb * 4 + q4) * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dv[nb][4 * q4 + e] += pv4[e];
-      }
-    }
-    store_tile_rows<T>(dv, 1.f, (uint16_t*)a.dv + row0 * HD, nrows, stage, lane);
+    store_tile_rows<T>(keep, mul, (uint16_t*)(qh == 0 ? a.dk : a.dv) + row0 * HD, nrows, stage, lane);
   }
 }
 
