@@ -108,12 +108,16 @@ struct BlockGroupSource {
   }
   __device__ void start() {
     const size_t row = row0 + (size_t)head * nkb;
+    // The row's entry `skip` is read together with its count (it is the walk's first entry
+    // whenever the row has more than `skip` entries; in bounds either way).
+    const int first = ((const_int_ptr)sel_k)[row * nqb + min(skip, nqb - 1)];
     const int n = cnt_k[row];
     const int s0 = min(skip, n);
     const int take = min(n - s0, left);
+    walk = TileWalker(sel_k + row * nqb + s0, take, bx, sq);
+    if (s0 == skip && take > 0) walk.pj = first;
     skip -= s0;
     left -= take;
-    walk = TileWalker(sel_k + row * nqb + s0, take, bx, sq);
   }
   __device__ bool next(int& hd, int& tile, uint64_t& bits) {
     while (true) {

@@ -115,7 +115,7 @@ struct TileWalker {
   const_int_ptr sel;
   int cnt, blk, len;
   int idx, last;
-  int pj;   // whole-tile walk: entry(idx), loaded by the previous call (pj < 0: not loaded)
+  int pj;   // entry(idx) when already loaded (whole-tile walk only; pj < 0: not loaded)
   __device__ TileWalker(const int* sel_, int cnt_, int blk_, int len_)
       : sel((const_int_ptr)sel_), cnt(cnt_), blk(blk_), len(len_), idx(0), last(-1), pj(-1) {}
   // Entry k of the list (wave-uniform k < cnt).
