@@ -51,20 +51,29 @@ struct WindowSource {
   }
 };
 
-// Tiles [tlo, thi) from the last one down, each over the heads [head0, head0 + nheads).  The
-// dK/dV workgroups of one kv head (all on one XCD) then read the same query tile at the same
-// time wherever their live ranges overlap (for causal masks they all end at the last tile).
+// Tiles [tlo, tlo + nt) from the last one down, each over the heads [head0, head0 + nheads)
+// (tiles outer), or every tile of a head before the next head (heads outer).  The dK/dV
+// workgroups of one kv head (all on one XCD) then read the same query tiles at about the same
+// time: tiles outer on wide windows (for causal masks every walk ends at the last tile);
+// heads outer on narrow windows, where neighbouring key tiles see overlapping runs of a few
+// query tiles and one head's run for all resident workgroups fits the XCD's L2.
 struct WindowSourceDesc {
-  int head0, hend, tlo, tile, head;
-  __device__ static WindowSourceDesc make(int head0, int nheads, int tlo, int nt) {
-    return WindowSourceDesc{head0, head0 + nheads, tlo, tlo + nt - 1, head0};
+  int head0, hend, tlo, thi, tile, head;
+  bool heads_outer;   // narrow windows: every tile of a head, then the next head
+  __device__ static WindowSourceDesc make(int head0, int nheads, int tlo, int nt, bool heads_outer = false) {
+    return WindowSourceDesc{head0, head0 + nheads, tlo, tlo + nt - 1, tlo + nt - 1, head0, heads_outer};
   }
   __device__ bool next(int& hd, int& t, uint64_t& bits) {
-    if (tile < tlo) return false;
+    if (tile < tlo || head >= hend) return false;
     hd = head;
     t = tile;
     bits = 0;
-    if (++head >= hend) {
+    if (heads_outer) {
+      if (--tile < tlo) {
+        tile = thi;
+        ++head;
+      }
+    } else if (++head >= hend) {
       head = head0;
       --tile;
     }
@@ -275,7 +284,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     const int qend = min(sq, c0 + BC + a.window - 1);
     const int tlo = c0 >> 6;
     const int thi = (qend + 63) >> 6;
-    wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo));
+    // Narrow windows (64-row key tiles, a few query tiles each): heads outer, so that the
+    // workgroups of neighbouring key tiles (one XCD) read the same head's query tiles at the
+    // same time and share them in L2; wide windows: tiles outer (comment above).
+    wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo), NK <= 2);
   } else {
     if (a.chunk > 0) bsrc.init(a, b, kvh, kblock, chunk * a.chunk, a.chunk);
     else bsrc.init(a, b, kvh, kblock, 0, 0x7fffffff);
