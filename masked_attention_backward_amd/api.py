@@ -143,6 +143,18 @@ def _workspace(nbytes, device, given=None):
     return given
 
 
+def _default_workspace(bank_bytes, min_bytes, device):
+    """The workspace a call allocates when the caller gives none: the dS-bank size, unless that
+    would take more than half of the device's free memory, then the minimum size (the library
+    then recomputes S and dP for dQ instead of reading dS back)."""
+    bank_bytes, min_bytes = int(bank_bytes), int(min_bytes)
+    if bank_bytes > min_bytes:
+        free, _ = torch.cuda.mem_get_info(device)
+        if bank_bytes > free // 2:
+            bank_bytes = min_bytes
+    return _workspace(bank_bytes, device)
+
+
 # --------------------------------------------------------------------------- sink path
 
 def attn_sink_fwd(q, k, v, sink, window, scale=None):
@@ -174,7 +186,8 @@ def attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, window, D=128):
 def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None, return_delta=False):
     """Backward with sink and sliding window -> (dq, dk, dv, dsink) [+ delta if return_delta].
     Without a workspace one of attn_sink_bwd_ds_workspace_bytes() is allocated (the dS-bank
-    path); a caller workspace of attn_sink_bwd_workspace_bytes() selects the recompute path."""
+    path), or of the minimum size when the bank would take more than half of the free device
+    memory; a caller workspace of attn_sink_bwd_workspace_bytes() selects the recompute path."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     dev = q.device
@@ -186,7 +199,8 @@ def attn_sink_bwd(q, k, v, o, do, lse, sink, window, scale=None, workspace=None,
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D), dev, workspace) if workspace is not None \
-        else _workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, window, D), dev)
+        else _default_workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, window, D),
+                                attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -265,7 +279,8 @@ def attn_sink_bwd_varlen(q, k, v, o, do, lse, sink, cu_seqlens, max_seqlen, wind
     _need(sink, "sink", (Hq,), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ws = _workspace(attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D), dev, workspace) if workspace is not None \
-        else _workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, smax, window, D), dev)
+        else _default_workspace(attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, smax, window, D),
+                                attn_sink_bwd_workspace_bytes(B, Hq, Hkv, smax, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -340,7 +355,8 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     """Block-sparse backward -> (dq, dk, dv); k/v (and dk/dv) may have fewer heads (GQA).
 
     Without a workspace one of blocksparse_attn_bwd_ds_workspace_bytes() is allocated (the
-    dS-bank path when bx and by are multiples of 32); a caller workspace of
+    dS-bank path when bx and by are multiples of 32), or of the minimum size when the bank would
+    take more than half of the free device memory; a caller workspace of
     blocksparse_attn_bwd_workspace_bytes() selects the recompute path."""
     B, N, Nkv, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
     dev = q.device
@@ -351,7 +367,8 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     _need(lse, "lse", (B, N, Sq), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ws = _workspace(blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev, workspace) \
-        if workspace is not None else _workspace(blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev)
+        if workspace is not None else _default_workspace(blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, bx, by, D),
+                                                         blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, bx, by, D), dev)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
