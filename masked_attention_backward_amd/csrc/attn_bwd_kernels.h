@@ -380,7 +380,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
   TileRef cur{};
   bool vcur = fetch(cur);
   if (vcur) issue(cur, 0);
-  int it = 0, stg = 0;
+  int it = 0;
   // Tiles where every (q, kv) of the workgroup is visible need no mask (rows past the
   // sequence end need none either: lse2 = +inf there; key columns past the end are never
   // stored).
@@ -390,249 +390,254 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     else
       return cur.bits == ~0ull;
   };
-  while (vcur) {
-    const bool masked = !is_full();
-    // This tile's loads (and, first time round, K/V) landed; with two stages the other stage
-    // is free once every wave has passed the barrier.
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (it == 0) {
-      negate_v();
+  // One visit; the stage is a template constant (two stages: the loop alternates two copies).
+  auto visit = [&](auto stc) {
+    constexpr int stg = decltype(stc)::value;
+      const bool masked = !is_full();
+      // This tile's loads (and, first time round, K/V) landed; with two stages the other stage
+      // is free once every wave has passed the barrier.
+      wait_vmcnt<0>();
       __syncthreads();
-    }
-    const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
-    // The next tile.  One stage: found before this tile's LDS reads are issued (a table entry
-    // read on the block path is a scalar load, whose wait would otherwise cover those reads as
-    // well); two stages: found, and its loads issued, once the first reads are in flight.
-    TileRef nxr{};
-    bool vn = false;
-    if constexpr (NSTAGE == 1) vn = fetch(nxr);
+      if (it == 0) {
+        negate_v();
+        __syncthreads();
+      }
+      const float* ld = sld + stg * 128 + qh * 32 + 4 * h;   // lse2 row; Delta row at +64
+      // This tile's stage: a compile-time offset on every fragment read (the loop body exists
+      // once per stage), so the lane offsets never change.
+      const uint16_t* const sb = stages + stg * (STAGE_BYTES / 2);
+      // The next tile.  One stage: found before this tile's LDS reads are issued (a table entry
+      // read on the block path is a scalar load, whose wait would otherwise cover those reads as
+      // well); two stages: found, and its loads issued, once the first reads are in flight.
+      TileRef nxr{};
+      bool vn = false;
+      if constexpr (NSTAGE == 1) vn = fetch(nxr);
 
-    // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
-    typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
-    f32x16 s, d;
-    {
-      // Delta of this wave's 32 query rows in accumulator order (register r = 4 g + e).
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[4 * g + e] = D4[e];
+      // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 key rows.
+      typedef const __attribute__((address_space(3))) f32x4* lds_f32x4;
+      f32x16 s, d;
+      {
+        // Delta of this wave's 32 query rows in accumulator order (register r = 4 g + e).
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) d[4 * g + e] = D4[e];
+        }
       }
-    }
-    u32x4 fq[2], fk[2], fd[2], fv[2];
-    // Every operand is read one k-step (two MFMAs) before its MFMA; the loads of the next tile
-    // are issued while the first reads are in flight.
-    fq[0] = frag_row(stages, fo, 0, 0, 0);
-    fk[0] = frag_row(kvs, fkv, 0, 0, 0);
-    fd[0] = frag_row(stages, fo, 1, 0, 0);
-    fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
-    if constexpr (NSTAGE == 2) {
-      vn = fetch(nxr);
-      if (vn) issue(nxr, stg ^ 1);
-    }
-    MA_STEP();
-    static_for<0, 8>([&](auto kc) {
-      constexpr int ks = decltype(kc)::value;
-      if constexpr (ks + 1 < 8) {
-        fq[(ks + 1) & 1] = frag_row(stages, fo, 0, ks + 1, 0);
-        fk[(ks + 1) & 1] = frag_row(kvs, fkv, 0, ks + 1, 0);
+      u32x4 fq[2], fk[2], fd[2], fv[2];
+      // Every operand is read one k-step (two MFMAs) before its MFMA; the loads of the next tile
+      // are issued while the first reads are in flight.
+      fq[0] = frag_row(sb, fo, 0, 0, 0);
+      fk[0] = frag_row(kvs, fkv, 0, 0, 0);
+      fd[0] = frag_row(sb, fo, 1, 0, 0);
+      fv[0] = frag_row(kvs, fkv, Sh::KV_TILES, 0, 0);
+      if constexpr (NSTAGE == 2) {
+        vn = fetch(nxr);
+        if (vn) issue(nxr, stg ^ 1);
       }
-      s = T::mma(fq[ks & 1], fk[ks & 1], ks ? s : zero16());
       MA_STEP();
-      if constexpr (ks + 1 < 8) {
-        fd[(ks + 1) & 1] = frag_row(stages, fo, 1, ks + 1, 0);
-        fv[(ks + 1) & 1] = frag_row(kvs, fkv, Sh::KV_TILES, ks + 1, 0);
-      }
-      d = T::mma(fd[ks & 1], fv[ks & 1], d);
-      MA_STEP();
-    });
-    if (masked) {
-      if constexpr (MASK == MASK_WINDOW) {
-        const int qdiff = cur.tile * 64 + qh * 32 + 4 * h - kj;
-        static_for<0, 16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          constexpr int qo = 8 * (r / 4) + (r % 4);
-          s[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s[r] : -INFINITY;
-        });
-      } else {
-        const uint64_t hb = cur.bits >> (qh * 32 + 4 * h);
-        static_for<0, 16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          constexpr int qo = 8 * (r / 4) + (r % 4);
-          s[r] = ((hb >> qo) & 1ull) ? s[r] : -INFINITY;
-        });
-      }
-    }
-    MA_STEP();
-    // log2 P = S scale log2e - lse log2e, in place.
-    {
-      f32x4 L[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], sl2, -L[r / 4][r % 4]);
-    }
-    // First dV/dK operands, read before the softmax rows that precede their MFMAs.
-    u32x4 fb[2], fc[2];
-    fb[0] = frag_col(stages, fo, 1, 0, 0);
-    fc[0] = frag_col(stages, fo, 0, 0, 0);
-    // P and dS enter the dV and dK products rounded to 16 bits.  Where some P of this wave's
-    // 32 x 32 block exceeds 1/4, the rounding error of such large terms, summed over every
-    // query row and head that attends strongly to one key, can approach the tolerance; those
-    // blocks (rare: the first query rows of a sequence, sharply peaked rows) also add the
-    // rounding residuals in a second product at the end of the tile (the page's compensated
-    // hi + lo GEMM), which makes their P and dS exact to about 22 bits.  The test is a
-    // ballot, uniform over the wave, so results stay deterministic.
-    float lmax = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, s[r]);
-    const bool comp = __builtin_amdgcn_ballot_w64(lmax > -2.0f) != 0;
-    MA_STEP();
-    // dS bank (window path): this wave's block, query block 2 tile + qh and key block
-    // c0 / 32 + kb, is stored when it holds a visible pair (the bank's band), as this wave
-    // holds it: the two A operands of the dK product, stored as soon as they are packed, so
-    // that the stores complete under this tile's dV/dK MFMAs (stores count in vmcnt, which
-    // the next tile's first wait drains).  Non-temporal: the bank is read once, by the dQ
-    // kernel, and should not displace the query tiles the other workgroups still read.
-    bool ds_live = false;   // wave-uniform
-    bool ds_edge = false;   // wave-uniform: the block reaches past the last key row
-    u32x4* ds_dst = nullptr;
-    if constexpr (MASK == MASK_BLOCK && DS) {
-      // Block path (block sizes multiples of 32, so this wave's 32 x 32 block lies inside one
-      // mask block): entry (head, qa, ka) of the dense grid, stored when some of its query
-      // rows are selected; key columns past the last key row are stored as zeros.
-      const int qa = 2 * cur.tile + qh, ka = (c0 >> 5) + kb;
-      ds_live = ((cur.bits >> (32 * qh)) & 0xffffffffull) != 0 && ka * 32 < kv_end;
-      ds_edge = ka * 32 + 32 > kv_end;
-      const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + (qa * a.ds_nka + ka);
-      ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
-    }
-    if constexpr (MASK == MASK_WINDOW && DS) {
-      const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
-      ds_live = kbk <= qa && qa - a.ds_kb <= kbk && qa * 32 < sq;
-      // Entry within the head in 32-bit arithmetic (the launcher keeps a head's bank below
-      // 2^30 blocks), the head's base in 64-bit.
-      const int off = band_offset32(qa, a.ds_kb) + kbk - max(0, qa - a.ds_kb);
-      const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + off;
-      ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
-    }
-    // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
-    // done one per MFMA between those eight MFMAs (with a dS bank, all sixteen up front, so
-    // both bank stores go out before the dV/dK MFMAs and complete under them: the next tile's
-    // first wait covers stores as well as loads).
-    constexpr bool ROWS_UP_FRONT = DS;
-    u32x4 pa[2], da[2];
-    float pk = 0.f, dk2 = 0.f;
-    auto srow = [&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      const float v = fast_exp2(s[r]);
-      const float dsv = -(v * d[r]);
-      if constexpr ((r & 1) == 0) {
-        pk = v;
-        dk2 = dsv;
-      } else {
-        pa[r / 8][(r % 8) / 2] = T::pack2(pk, v);
-        da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
-      }
-    };
-    static_for<0, ROWS_UP_FRONT ? 16 : 8>(srow);
-    if constexpr (ROWS_UP_FRONT) {
-      if (MASK == MASK_BLOCK && ds_edge && kj >= kv_end) {
-        // Key rows past the end: dS of these columns is garbage computed on clamped K rows;
-        // zero it (it only feeds dK rows that are never stored, and the dQ product).
-        da[0] = (u32x4){0u, 0u, 0u, 0u};
-        da[1] = (u32x4){0u, 0u, 0u, 0u};
-      }
-      if (ds_live) {
-        __builtin_nontemporal_store(da[0], ds_dst);
-        __builtin_nontemporal_store(da[1], ds_dst + 64);
-      }
-    }
-    // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows.
-    MA_STEP();
-    static_for<0, 8>([&](auto jc) {
-      constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
-      if constexpr (j + 1 < 8) {
-        fb[(j + 1) & 1] = frag_col(stages, fo, 1, (j + 1) / 4, (j + 1) % 4);
-        fc[(j + 1) & 1] = frag_col(stages, fo, 0, (j + 1) / 4, (j + 1) % 4);
-      }
-      dv[nb] = T::mma(pa[t], fb[j & 1], dv[nb]);
-      if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 8 + 2 * j>{});
-      MA_STEP();
-      dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
-      if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 9 + 2 * j>{});
-      MA_STEP();
-    });
-    if (comp) {
-      // Residual products of this tile: S and dP again from the stage (still resident), the
-      // same mask and exponent, then dV += (P - hi(P))^T dO and dK += (dS - hi(dS))^T Q.
-      f32x16 s2 = zero16(), d2;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d2[4 * g + e] = D4[e];
-      }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s2 = T::mma(frag_row(stages, fo, 0, ks, 0), frag_row(kvs, fkv, 0, ks, 0), s2);
-        d2 = T::mma(frag_row(stages, fo, 1, ks, 0), frag_row(kvs, fkv, Sh::KV_TILES, ks, 0), d2);
-      }
+      static_for<0, 8>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 1 < 8) {
+          fq[(ks + 1) & 1] = frag_row(sb, fo, 0, ks + 1, 0);
+          fk[(ks + 1) & 1] = frag_row(kvs, fkv, 0, ks + 1, 0);
+        }
+        s = T::mma(fq[ks & 1], fk[ks & 1], ks ? s : zero16());
+        MA_STEP();
+        if constexpr (ks + 1 < 8) {
+          fd[(ks + 1) & 1] = frag_row(sb, fo, 1, ks + 1, 0);
+          fv[(ks + 1) & 1] = frag_row(kvs, fkv, Sh::KV_TILES, ks + 1, 0);
+        }
+        d = T::mma(fd[ks & 1], fv[ks & 1], d);
+        MA_STEP();
+      });
       if (masked) {
         if constexpr (MASK == MASK_WINDOW) {
           const int qdiff = cur.tile * 64 + qh * 32 + 4 * h - kj;
           static_for<0, 16>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
             constexpr int qo = 8 * (r / 4) + (r % 4);
-            s2[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s2[r] : -INFINITY;
+            s[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s[r] : -INFINITY;
           });
         } else {
           const uint64_t hb = cur.bits >> (qh * 32 + 4 * h);
           static_for<0, 16>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
             constexpr int qo = 8 * (r / 4) + (r % 4);
-            s2[r] = ((hb >> qo) & 1ull) ? s2[r] : -INFINITY;
+            s[r] = ((hb >> qo) & 1ull) ? s[r] : -INFINITY;
           });
         }
       }
-      u32x4 pl[2], dl[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 L4 = *(lds_f32x4)(ld + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r = 4 * g + e;
-          const float v0 = fast_exp2(fmaf(s2[r], sl2, -L4[e]));
-          const float v1 = fast_exp2(fmaf(s2[r + 1], sl2, -L4[e + 1]));
-          const float d0 = -(v0 * d2[r]), d1 = -(v1 * d2[r + 1]);
-          const uint32_t ph = T::pack2(v0, v1), dh = T::pack2(d0, d1);
-          pl[r / 8][(r % 8) / 2] = T::pack2(v0 - T::lo(ph), v1 - T::hi(ph));
-          dl[r / 8][(r % 8) / 2] = T::pack2(d0 - T::lo(dh), d1 - T::hi(dh));
+      MA_STEP();
+      // log2 P = S scale log2e - lse log2e, in place.
+      {
+        f32x4 L[4];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) L[g] = *(lds_f32x4)(ld + 8 * g);
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], sl2, -L[r / 4][r % 4]);
+      }
+      // First dV/dK operands, read before the softmax rows that precede their MFMAs.
+      u32x4 fb[2], fc[2];
+      fb[0] = frag_col(sb, fo, 1, 0, 0);
+      fc[0] = frag_col(sb, fo, 0, 0, 0);
+      // P and dS enter the dV and dK products rounded to 16 bits.  Where some P of this wave's
+      // 32 x 32 block exceeds 1/4, the rounding error of such large terms, summed over every
+      // query row and head that attends strongly to one key, can approach the tolerance; those
+      // blocks (rare: the first query rows of a sequence, sharply peaked rows) also add the
+      // rounding residuals in a second product at the end of the tile (the page's compensated
+      // hi + lo GEMM), which makes their P and dS exact to about 22 bits.  The test is a
+      // ballot, uniform over the wave, so results stay deterministic.
+      float lmax = s[0];
+  #pragma unroll
+      for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, s[r]);
+      const bool comp = __builtin_amdgcn_ballot_w64(lmax > -2.0f) != 0;
+      MA_STEP();
+      // dS bank (window path): this wave's block, query block 2 tile + qh and key block
+      // c0 / 32 + kb, is stored when it holds a visible pair (the bank's band), as this wave
+      // holds it: the two A operands of the dK product, stored as soon as they are packed, so
+      // that the stores complete under this tile's dV/dK MFMAs (stores count in vmcnt, which
+      // the next tile's first wait drains).  Non-temporal: the bank is read once, by the dQ
+      // kernel, and should not displace the query tiles the other workgroups still read.
+      bool ds_live = false;   // wave-uniform
+      bool ds_edge = false;   // wave-uniform: the block reaches past the last key row
+      u32x4* ds_dst = nullptr;
+      if constexpr (MASK == MASK_BLOCK && DS) {
+        // Block path (block sizes multiples of 32, so this wave's 32 x 32 block lies inside one
+        // mask block): entry (head, qa, ka) of the dense grid, stored when some of its query
+        // rows are selected; key columns past the last key row are stored as zeros.
+        const int qa = 2 * cur.tile + qh, ka = (c0 >> 5) + kb;
+        ds_live = ((cur.bits >> (32 * qh)) & 0xffffffffull) != 0 && ka * 32 < kv_end;
+        ds_edge = ka * 32 + 32 > kv_end;
+        const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + (qa * a.ds_nka + ka);
+        ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
+      }
+      if constexpr (MASK == MASK_WINDOW && DS) {
+        const int qa = 2 * cur.tile + qh, kbk = (c0 >> 5) + kb;
+        ds_live = kbk <= qa && qa - a.ds_kb <= kbk && qa * 32 < sq;
+        // Entry within the head in 32-bit arithmetic (the launcher keeps a head's bank below
+        // 2^30 blocks), the head's base in 64-bit.
+        const int off = band_offset32(qa, a.ds_kb) + kbk - max(0, qa - a.ds_kb);
+        const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + off;
+        ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
+      }
+      // Rows 0-7 feed the first four dV/dK k-step pairs and are done up front; rows 8-15 are
+      // done one per MFMA between those eight MFMAs (with a dS bank, all sixteen up front, so
+      // both bank stores go out before the dV/dK MFMAs and complete under them: the next tile's
+      // first wait covers stores as well as loads).
+      constexpr bool ROWS_UP_FRONT = DS;
+      u32x4 pa[2], da[2];
+      float pk = 0.f, dk2 = 0.f;
+      auto srow = [&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const float v = fast_exp2(s[r]);
+        const float dsv = -(v * d[r]);
+        if constexpr ((r & 1) == 0) {
+          pk = v;
+          dk2 = dsv;
+        } else {
+          pa[r / 8][(r % 8) / 2] = T::pack2(pk, v);
+          da[r / 8][(r % 8) / 2] = T::pack2(dk2, dsv);
+        }
+      };
+      static_for<0, ROWS_UP_FRONT ? 16 : 8>(srow);
+      if constexpr (ROWS_UP_FRONT) {
+        if (MASK == MASK_BLOCK && ds_edge && kj >= kv_end) {
+          // Key rows past the end: dS of these columns is garbage computed on clamped K rows;
+          // zero it (it only feeds dK rows that are never stored, and the dQ product).
+          da[0] = (u32x4){0u, 0u, 0u, 0u};
+          da[1] = (u32x4){0u, 0u, 0u, 0u};
+        }
+        if (ds_live) {
+          __builtin_nontemporal_store(da[0], ds_dst);
+          __builtin_nontemporal_store(da[1], ds_dst + 64);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = j / 4, nb = j % 4;
-        dv[nb] = T::mma(pl[t], frag_col(stages, fo, 1, t, nb), dv[nb]);
-        dk[nb] = T::mma(dl[t], frag_col(stages, fo, 0, t, nb), dk[nb]);
+      // dV += P^T dO, dK += dS^T Q over this wave's 32 query rows.
+      MA_STEP();
+      static_for<0, 8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, t = j / 4, nb = j % 4;
+        if constexpr (j + 1 < 8) {
+          fb[(j + 1) & 1] = frag_col(sb, fo, 1, (j + 1) / 4, (j + 1) % 4);
+          fc[(j + 1) & 1] = frag_col(sb, fo, 0, (j + 1) / 4, (j + 1) % 4);
+        }
+        dv[nb] = T::mma(pa[t], fb[j & 1], dv[nb]);
+        if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 8 + 2 * j>{});
+        MA_STEP();
+        dk[nb] = T::mma(da[t], fc[j & 1], dk[nb]);
+        if constexpr (j < 4 && !ROWS_UP_FRONT) srow(std::integral_constant<int, 9 + 2 * j>{});
+        MA_STEP();
+      });
+      if (comp) {
+        // Residual products of this tile: S and dP again from the stage (still resident), the
+        // same mask and exponent, then dV += (P - hi(P))^T dO and dK += (dS - hi(dS))^T Q.
+        f32x16 s2 = zero16(), d2;
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 D4 = *(lds_f32x4)(ld + 64 + 8 * g);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) d2[4 * g + e] = D4[e];
+        }
+  #pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          s2 = T::mma(frag_row(sb, fo, 0, ks, 0), frag_row(kvs, fkv, 0, ks, 0), s2);
+          d2 = T::mma(frag_row(sb, fo, 1, ks, 0), frag_row(kvs, fkv, Sh::KV_TILES, ks, 0), d2);
+        }
+        if (masked) {
+          if constexpr (MASK == MASK_WINDOW) {
+            const int qdiff = cur.tile * 64 + qh * 32 + 4 * h - kj;
+            static_for<0, 16>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              constexpr int qo = 8 * (r / 4) + (r % 4);
+              s2[r] = ((unsigned)(qdiff + qo) < (unsigned)a.window) ? s2[r] : -INFINITY;
+            });
+          } else {
+            const uint64_t hb = cur.bits >> (qh * 32 + 4 * h);
+            static_for<0, 16>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              constexpr int qo = 8 * (r / 4) + (r % 4);
+              s2[r] = ((hb >> qo) & 1ull) ? s2[r] : -INFINITY;
+            });
+          }
+        }
+        u32x4 pl[2], dl[2];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 L4 = *(lds_f32x4)(ld + 8 * g);
+  #pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const int r = 4 * g + e;
+            const float v0 = fast_exp2(fmaf(s2[r], sl2, -L4[e]));
+            const float v1 = fast_exp2(fmaf(s2[r + 1], sl2, -L4[e + 1]));
+            const float d0 = -(v0 * d2[r]), d1 = -(v1 * d2[r + 1]);
+            const uint32_t ph = T::pack2(v0, v1), dh = T::pack2(d0, d1);
+            pl[r / 8][(r % 8) / 2] = T::pack2(v0 - T::lo(ph), v1 - T::hi(ph));
+            dl[r / 8][(r % 8) / 2] = T::pack2(d0 - T::lo(dh), d1 - T::hi(dh));
+          }
+        }
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = j / 4, nb = j % 4;
+          dv[nb] = T::mma(pl[t], frag_col(sb, fo, 1, t, nb), dv[nb]);
+          dk[nb] = T::mma(dl[t], frag_col(sb, fo, 0, t, nb), dk[nb]);
+        }
       }
-    }
+      if constexpr (NSTAGE == 1) {
+        // One stage: every wave is done reading it before the next tile's loads overwrite it.
+        __syncthreads();
+        if (vn) issue(nxr, 0);
+      }
+      cur = nxr;
+      vcur = vn;
+      ++it;
+  };
+  while (vcur) {
+    visit(std::integral_constant<int, 0>{});
     if constexpr (NSTAGE == 2) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        fo.row[i] ^= STAGE_BYTES;
-        fo.col[i] ^= STAGE_BYTES;
-      }
-      stg ^= 1;
-    } else {
-      // One stage: every wave is done reading it before the next tile's loads overwrite it.
-      __syncthreads();
-      if (vn) issue(nxr, 0);
+      if (!vcur) break;
+      visit(std::integral_constant<int, 1>{});
     }
-    cur = nxr;
-    vcur = vn;
-    ++it;
   }
   wait_vmcnt<0>();   // K/V loads when there was no tile at all
   __syncthreads();
