@@ -105,7 +105,17 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
  * for every 32 x 32 (query block, key block) pair holding a visible (i, j) of each (batch,
  * query head): B * Hq * sum_a (min(a, kb) + 1) blocks, a over ceil(S/32) query blocks, kb =
  * ceil((min(window, S) - 1) / 32).  For window = S that is the lower triangle: 4.3 GB at
- * B = 1, Hq = 64, S = 8192. */
+ * B = 1, Hq = 64, S = 8192.
+ * Wide windows (W = min(window, S) >= 256 and 4 W >= S) whose ceil(S/128) key tiles of 128
+ * rows give B * Hkv * ceil(ceil(S/128) / 2) < 256 tile pairs: the bank is followed (at the
+ * next 256-byte boundary) by the fp32 partial dK and dV of a head split of the dK/dV work,
+ * 2 * B * Hkv * M * Sp * D * 4 bytes.  Key tile p's visits (its query heads times the 64-row
+ * query tiles of rows [128 p, min(S, 128 p + 127 + W))) go to min(group, ceil(visits /
+ * target)) workgroups of whole query heads, target = max(16, ceil(all tiles' visits * B *
+ * Hkv / 1024)), M the largest such count (none when M = 1); the partial sums are added in
+ * chunk order (deterministic).  268 MB at B = 1, Hq = 64, Hkv = 8, S = window = 4096 (M = 8;
+ * the key tiles near the start see up to twice the average work).  Dense calls only: the
+ * packed-sequence entry points do not split. */
 size_t attn_sink_bwd_ds_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int window);
 
 /* ---------------------------------------------------------------------------------

@@ -118,15 +118,17 @@ __global__ __launch_bounds__(64) void dsink_reduce_kernel(const float* __restric
   if (lane == 0) dsink[h] = -acc;
 }
 
-// Block path, key blocks whose selected query blocks span several dK/dV workgroups: sum the
-// fp32 partials in chunk order (fixed, so results are bit-identical run to run) and cast.
-// A 256-thread block covers 8 key rows x 128 columns (4 columns per thread) of one kv head.
-template <class T>
+// Key blocks (block path) or key tiles (window path, head split) whose dK/dV sums span several
+// workgroups: sum the fp32 partials in chunk order (fixed, so results are bit-identical run to
+// run) and cast.  A 256-thread block covers 8 key rows x 128 columns (4 columns per thread) of
+// one kv head.
+template <class T, int MASK>
 __global__ __launch_bounds__(256) void dkv_chunk_reduce_kernel(const AttnArgs a) {
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int row = blockIdx.x * 8 + (threadIdx.x >> 5), col = (threadIdx.x & 31) * 4;
   if (row >= a.Skv) return;
-  const int nch = block_chunks(a, b, kvh, row / a.by);
+  const int nch = MASK == MASK_WINDOW ? window_chunks(a.Sq, a.window, a.group, a.chunk, row / 128)
+                                      : block_chunks(a, b, kvh, row / a.by);
   if (nch <= 1) return;   // stored directly by its only workgroup
   const int skv_pad = (a.Skv + 63) & ~63;
   const size_t slot = (size_t)skv_pad * HD;
@@ -196,9 +198,13 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   aq.n_tiles = (a.Sq + 32 * aq.dq_nw - 1) / (32 * aq.dq_nw);
   const int pairs_dkdv = a.B * a.Hkv * ((nt + 1) / 2);
   const int pairs_dq = a.B * a.Hq * ((aq.n_tiles + 1) / 2);
-  ak.pair = (wide && pairs_dkdv >= 256) ? 1 : 0;
+  // Head split (planned by the caller for dense wide windows whose tiles cannot be paired):
+  // max_chunks slots per key tile, the partial sums added by the chunk reduce.
+  const bool split = wide && !a.cu && a.max_chunks > 1;
+  if (!split) ak.max_chunks = 1;
+  ak.pair = (!split && wide && pairs_dkdv >= 256) ? 1 : 0;
   aq.pair = (wide && pairs_dq >= 256) ? 1 : 0;
-  const int gk = a.B * a.Hkv * (ak.pair ? (ak.n_tiles + 1) / 2 : ak.n_tiles);
+  const int gk = a.B * a.Hkv * (split ? ak.n_tiles * ak.max_chunks : ak.pair ? (ak.n_tiles + 1) / 2 : ak.n_tiles);
   const int gq = a.B * a.Hq * (aq.pair ? (aq.n_tiles + 1) / 2 : aq.n_tiles);
   if (wide) {
     if (dtype == 1) launch_dkdv_variant<BF16, MASK_WINDOW, 4>(ak, gk, st);
@@ -206,6 +212,11 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   } else {
     if (dtype == 1) launch_dkdv_variant<BF16, MASK_WINDOW, 2>(ak, gk, st);
     else launch_dkdv_variant<F16, MASK_WINDOW, 2>(ak, gk, st);
+  }
+  if (split) {
+    const dim3 grid((a.Skv + 7) / 8, a.Hkv, a.B);
+    if (dtype == 1) hipLaunchKernelGGL((dkv_chunk_reduce_kernel<BF16, MASK_WINDOW>), grid, dim3(256), 0, st, ak);
+    else hipLaunchKernelGGL((dkv_chunk_reduce_kernel<F16, MASK_WINDOW>), grid, dim3(256), 0, st, ak);
   }
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   if (dtype == 1) launch_dq_variant<BF16, MASK_WINDOW, 4>(aq, gq, st);
@@ -224,7 +235,8 @@ static void launch_block_t(const AttnArgs& a, hipStream_t st, hipEvent_t ev_mid)
     default: launch_dkdv_variant<T, MASK_BLOCK, 4>(a, gk, st); break;
   }
   if (a.max_chunks > 1)
-    hipLaunchKernelGGL(dkv_chunk_reduce_kernel<T>, dim3((a.Skv + 7) / 8, a.Hkv, a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dkv_chunk_reduce_kernel<T, MASK_BLOCK>), dim3((a.Skv + 7) / 8, a.Hkv, a.B), dim3(256), 0,
+                       st, a);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   switch (nwq) {
     case 1: launch_dq_variant<T, MASK_BLOCK, 1>(a, gq, st); break;

@@ -241,7 +241,8 @@ constexpr int dkdv_waves_per_simd() { return dkdv_stages<MASK, NK>() == 1 ? 2 : 
 
 template <class T, int MASK, int NK, bool DS = false>
 __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int c0, int kv_end, int kblock,
-                                          uint16_t* smem, int chunk = 0, bool partial = false) {
+                                          uint16_t* smem, int chunk = 0, bool partial = false, int hoff = 0,
+                                          int hcnt = 0) {
   constexpr int NSTAGE = dkdv_stages<MASK, NK>();
   using Sh = DkdvShape<NK, NSTAGE>;
   constexpr int NWV = Sh::NWAVES;
@@ -287,7 +288,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // Narrow windows (64-row key tiles, a few query tiles each): heads outer, so that the
     // workgroups of neighbouring key tiles (one XCD) read the same head's query tiles at the
     // same time and share them in L2; wide windows: tiles outer (comment above).
-    wsrc = WindowSourceDesc::make(kvh * a.group, a.group, tlo, max(0, thi - tlo), NK <= 2);
+    // A head split takes query heads hoff .. hoff + hcnt - 1 of the group only.
+    wsrc = WindowSourceDesc::make(kvh * a.group + hoff, hcnt > 0 ? hcnt : a.group, tlo, max(0, thi - tlo), NK <= 2);
   } else {
     if (a.chunk > 0) bsrc.init(a, b, kvh, kblock, chunk * a.chunk, a.chunk);
     else bsrc.init(a, b, kvh, kblock, 0, 0x7fffffff);
@@ -704,6 +706,19 @@ __global__ __launch_bounds__(2 * NK * 64, (dkdv_waves_per_simd<MASK, NK>())) voi
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BC = 32 * NK;
+    if constexpr (NK == 4) {
+      if (a.max_chunks > 1) {
+        // Head split (dense sequences, wide windows, too few tiles to pair): slot p holds chunk
+        // max_chunks - 1 - p / n_tiles of key tile p % n_tiles, so the extra chunks of the
+        // heaviest tiles are dispatched first; slots past a tile's chunk count return at once.
+        const int kt = p % a.n_tiles, c = a.max_chunks - 1 - p / a.n_tiles;
+        const int nch = window_chunks(a.Sq, a.window, a.group, a.chunk, kt);
+        if (c >= nch) return;   // uniform: no loads or barriers issued yet
+        const int h0 = c * a.group / nch, h1 = (c + 1) * a.group / nch;
+        dkdv_tile<T, MASK, NK, DS>(a, b, kvh, kt * BC, a.Skv, 0, smem, c, nch > 1, h0, h1 - h0);
+        return;
+      }
+    }
     // Workgroups of one (batch, kv head) are consecutive modulo B*Hkv: with B*Hkv = 8 they
     // all land on one XCD and share its L2.  Tile p is paired with tile n - 1 - p (equal
     // total work) when the launcher sets `pair`; n counts the tiles of this sequence, so a

@@ -193,10 +193,46 @@ static long long ds_kb_of(int S, int window) {
 }
 static long long ds_blocks_of(int S, int window) { return ma::band_offset((S + 31) / 32, ds_kb_of(S, window)); }
 
+// Head split of the dK/dV work on dense wide windows (128-row key tiles, window >= 256 and
+// 4 window >= S) whose tiles cannot be paired (fewer than 256 pairs): one workgroup per key
+// tile would leave the heaviest tile (the first, under a causal window) with about twice the
+// average work.  Each tile's visits (query heads x 64-row query tiles) are split over at most
+// `group` workgroups of whole heads, at most a quarter of a compute unit's share of all visits
+// each (at least 16; a half and an eighth measured slower on B1 H64 Hkv8 S4096); their fp32
+// partial sums are added in a fixed order.  max_chunks = 1: no split.
+struct WindowSplit {
+  int target, max_chunks;
+};
+static WindowSplit window_split(int B, int Hq, int Hkv, int S, int window) {
+  WindowSplit ws{0, 1};
+  const int W = window < S ? window : S;
+  if (!(W >= 256 && (long long)W * 4 >= S)) return ws;
+  const int nt = (S + 127) / 128;
+  const long long units = (long long)B * Hkv;
+  if (units * ((nt + 1) / 2) >= 256) return ws;
+  const int group = Hq / Hkv;
+  long long visits = 0;
+  for (int p = 0; p < nt; ++p) visits += (long long)group * ma::window_qtiles(S, W, p);
+  const long long t = (units * visits + 1023) / 1024;
+  ws.target = (int)(t < 16 ? 16 : t > (1ll << 30) ? (1ll << 30) : t);
+  for (int p = 0; p < nt; ++p) {
+    const int c = ma::window_chunks(S, W, group, ws.target, p);
+    if (c > ws.max_chunks) ws.max_chunks = c;
+  }
+  return ws;
+}
+// The split's partial sums: dK and dV, max_chunks slots of padded S rows x D fp32 per
+// (sequence, kv head).
+static size_t window_part_bytes(int B, int Hkv, int S, const WindowSplit& ws) {
+  if (ws.max_chunks <= 1) return 0;
+  return align256(2 * (size_t)B * Hkv * ws.max_chunks * pad64(S) * ma::HD * sizeof(float));
+}
+
 size_t attn_sink_bwd_ds_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int window) {
   const size_t base = attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, D);
   if (base == 0 || window < 1) return 0;
-  return base + align256((size_t)B * Hq * (size_t)ds_blocks_of(S, window) * 2048);
+  return base + align256((size_t)B * Hq * (size_t)ds_blocks_of(S, window) * 2048) +
+         window_part_bytes(B, Hkv, S, window_split(B, Hq, Hkv, S, window));
 }
 
 static int sink_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -245,6 +281,13 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
     a.ds_bank = at<uint16_t>(workspace, need);
     a.ds_kb = (int)ds_kb_of(S, window);
     a.ds_blocks = ds_blocks_of(S, window);
+    // The same workspace holds the head split's partial sums after the bank (dense sequences).
+    const WindowSplit ws = window_split(B, Hq, Hkv, S, window);
+    if (!cu && ws.max_chunks > 1) {
+      a.chunk = ws.target;
+      a.max_chunks = ws.max_chunks;
+      a.dkv_part = at<float>(workspace, need + align256((size_t)B * Hq * (size_t)ds_blocks_of(S, window) * 2048));
+    }
   }
   e = ma::launch_window_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);
   if (events) hipEventRecord((hipEvent_t)events[3], hs);

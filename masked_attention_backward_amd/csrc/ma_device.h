@@ -204,9 +204,11 @@ struct AttnArgs {
   int pair;              // 1: workgroup p also runs tile n_tiles-1-p
   const int* cu;         // packed sequences: [B + 1] row offsets (nullptr: dense [B, H, S, D])
   int total;             // packed sequences: rows per head of every tensor
-  int chunk;             // block path: selected query blocks per dK/dV workgroup (0: no limit)
-  int max_chunks;        // block path: chunks per (kv head, key block) the grid provides for
-  float* dkv_part;       // block path, chunked key blocks: fp32 partial dK (scaled) and dV,
+  int chunk;             // block path: selected query blocks per dK/dV workgroup (0: no limit);
+                         // window path with a head split: tile visits per dK/dV workgroup
+  int max_chunks;        // chunks per (kv head, key block or key tile) the dK/dV grid provides
+                         // for (1: no split)
+  float* dkv_part;       // split key blocks / tiles: fp32 partial dK (scaled) and dV,
                          // [2][B][Hkv][max_chunks][padded Skv][D]
   uint16_t* ds_bank;     // window path: dS of every live 32 x 32 block, written by dK/dV and
                          // read by the dQ GEMM (nullptr: dQ recomputes S and dP instead)
@@ -249,6 +251,21 @@ __device__ __forceinline__ int band_lo(int a, int kb) { return max(0, a - kb); }
 __device__ __host__ __forceinline__ long long band_offset(long long a, long long kb) {
   // sum over a' < a of (min(a', kb) + 1)
   return a <= kb + 1 ? a * (a + 1) / 2 : (kb + 1) * (kb + 2) / 2 + (a - kb - 1) * (kb + 1);
+}
+// Window path, wide windows (128-row key tiles): the 64-row query tiles key tile p visits
+// (rows [128 p, min(S, 128 p + 128 + W - 1)) of every query head of its group).
+__device__ __host__ __forceinline__ int window_qtiles(int S, int W, int p) {
+  const int c0 = p * 128;
+  const int qend = S < c0 + 128 + W - 1 ? S : c0 + 128 + W - 1;
+  const int n = ((qend + 63) >> 6) - (c0 >> 6);
+  return n > 0 ? n : 0;
+}
+// Head split of wide-window key tiles that cannot be paired: the workgroups key tile p's
+// visits (query heads x query tiles) are spread over, whole query heads each, at most
+// `target` visits per workgroup where the group allows (1: not split).
+__device__ __host__ __forceinline__ int window_chunks(int S, int W, int group, int target, int p) {
+  const int n = (group * window_qtiles(S, W, p) + target - 1) / target;
+  return n < 1 ? 1 : (n > group ? group : n);
 }
 // The same in 32-bit arithmetic, exact while the head's bank holds fewer than 2^30 blocks.
 __device__ __forceinline__ int band_offset32(int a, int kb) {

@@ -125,6 +125,41 @@ def test_ds_workspace_query(lib):
     assert lib.attn_sink_bwd_ds_workspace_bytes(1, 4, 1, 128, 64, 10) == 0
 
 
+def split_plan(B, Hq, Hkv, S, window):
+    """The head split of wide-window key tiles, derived from its stated rule: dense wide windows
+    (W >= 256, 4 W >= S) whose 128-row key tiles give fewer than 256 pairs; a key tile's visits
+    (query heads x 64-row query tiles of rows [128 p, min(S, 128 p + 127 + W))) split over at
+    most group workgroups of about max(16, ceil(all visits / 1024)) visits each."""
+    W = min(window, S)
+    nt = -(-S // 128)
+    if W < 256 or 4 * W < S or B * Hkv * -(-nt // 2) >= 256:
+        return 1
+    g = Hq // Hkv
+    qt = [len(range(128 * p // 64, -(-min(S, 128 * p + 127 + W) // 64))) for p in range(nt)]
+    target = max(16, -(-B * Hkv * g * sum(qt) // 1024))
+    return max(min(g, max(1, -(-g * n // target))) for n in qt)
+
+
+def test_ds_workspace_head_split(lib):
+    """Dense wide windows with too few key tiles to pair: the dS-bank workspace also holds the
+    head split's fp32 partial dK and dV (max_chunks slots of padded S x 128 per kv head)."""
+    Z, I = ctypes.c_size_t, ctypes.c_int
+    lib.attn_sink_bwd_workspace_bytes.restype = Z
+    lib.attn_sink_bwd_ds_workspace_bytes.restype = Z
+    lib.attn_sink_bwd_ds_workspace_bytes.argtypes = [I] * 6
+    seen_split = 0
+    for B, Hq, Hkv, S, W in [(1, 64, 8, 4096, 4096), (1, 8, 2, 600, 600), (1, 6, 2, 700, 400), (2, 8, 2, 1024, 1024),
+                             (1, 4, 4, 520, 300), (1, 64, 8, 8192, 8192), (1, 8, 1, 2048, 300), (4, 16, 16, 1024, 1024)]:
+        base = lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, 128)
+        bank = -(-B * Hq * brute_band_blocks(S, min(W, S)) * 2048 // 256) * 256
+        mc = split_plan(B, Hq, Hkv, S, W)
+        part = 0 if mc == 1 else -(-2 * B * Hkv * mc * (-(-S // 64) * 64) * 128 * 4 // 256) * 256
+        seen_split += mc > 1
+        assert lib.attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, 128, W) == base + bank + part, (B, Hq, Hkv, S, W)
+    assert split_plan(1, 64, 8, 4096, 4096) == 8 and split_plan(1, 64, 8, 8192, 8192) == 1
+    assert seen_split == 4
+
+
 def test_block_ds_workspace_query(lib):
     """The block path's dS-bank workspace: the minimum one plus 2048 bytes per cell of the
     dense grid of 32 x 32 blocks of every (batch, query head) when bx and by are multiples of

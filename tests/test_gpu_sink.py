@@ -107,6 +107,58 @@ def test_bwd_paired_tiles():
     check_all(wl, x, ref, delta=False)
 
 
+# Dense wide windows with too few 128-row key tiles to pair: with the dS-bank workspace the
+# heaviest key tiles are split by query heads over several dK/dV workgroups (fp32 partials,
+# added in chunk order).  Splits of 3 chunks over 4 heads (uneven), a sliding window, two
+# sequences and a ragged last key tile.
+HEAD_SPLIT = [
+    W.custom_sink("split_s600_causal", 1, 8, 2, 600, 600, torch.float16, seed_base=120),
+    W.custom_sink("split_s700_w400_bf16", 1, 6, 2, 700, 400, torch.bfloat16, seed_base=121),
+    W.custom_sink("split_b2_s1024_causal", 2, 8, 2, 1024, 1024, torch.float16, seed_base=122),
+]
+
+
+@pytest.mark.parametrize("wl", HEAD_SPLIT, ids=lambda w: w.name)
+def test_bwd_head_split(wl):
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check_all(wl, x, ref)
+
+
+def test_head_split_deterministic_and_fully_written():
+    """Head-split launch: three runs bit-identical; outputs and workspace (partials included)
+    pre-filled with 0xFF are fully overwritten / never read before written."""
+    wl = HEAD_SPLIT[0]
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    g = {k: v.to(DEV) for k, v in x.items()}
+    a = api()
+    nbytes = a.attn_sink_bwd_ds_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.window)
+    assert nbytes > a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq) + \
+        wl.B * wl.Hq * 2048 * ((wl.Sq + 31) // 32) * ((wl.Sq + 31) // 32 + 1) // 2   # partials present
+    outs = []
+    for _ in range(3):
+        dq = torch.full_like(g["q"], float("nan"))
+        dk = torch.full_like(g["k"], float("nan"))
+        dv = torch.full_like(g["v"], float("nan"))
+        dsink = torch.full((wl.Hq,), float("nan"), device=DEV)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+        print(f"[gpu] attn_sink_bwd (head split) {wl.name}", flush=True)
+        st = a.lib.attn_sink_bwd(*(ctypes.c_void_p(t.data_ptr()) for t in (
+            g["q"], g["k"], g["v"], g["o"], g["do"], g["lse"], g["sink"], dq, dk, dv, dsink, ws)),
+            nbytes, wl.B, wl.Hq, wl.Hkv, wl.Sq, 128, wl.window, wl.scale, a.MA_F16,
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv, dsink)])
+    for t in outs[0]:
+        assert torch.isfinite(t.float()).all()
+    for other in outs[1:]:
+        for u, v in zip(outs[0], other):
+            assert torch.equal(u.view(torch.int16) if u.dtype != torch.float32 else u.view(torch.int32),
+                               v.view(torch.int16) if v.dtype != torch.float32 else v.view(torch.int32))
+
+
 @pytest.mark.parametrize("wl", [SMALL[0], SMALL[2], SMALL[6], W.custom_sink("f_causal", 1, 4, 1, 333, 333,
                                                                              torch.float16, seed_base=112)],
                          ids=lambda w: w.name)
