@@ -106,7 +106,7 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
  * query head): B * Hq * sum_a (min(a, kb) + 1) blocks, a over ceil(S/32) query blocks, kb =
  * ceil((min(window, S) - 1) / 32).  For window = S that is the lower triangle: 4.3 GB at
  * B = 1, Hq = 64, S = 8192.
- * Wide windows (W = min(window, S) >= 256 and 4 W >= S) whose ceil(S/128) key tiles of 128
+ * Wide windows (W = min(window, S) >= 256) whose ceil(S/128) key tiles of 128
  * rows give B * Hkv * ceil(ceil(S/128) / 2) < 256 tile pairs: the bank is followed (at the
  * next 256-byte boundary) by the fp32 partial dK and dV of a head split of the dK/dV work,
  * 2 * B * Hkv * M * Sp * D * 4 bytes.  Key tile p's visits (its query heads times the 64-row

@@ -186,10 +186,11 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   // rows (dQ).  The work per tile grows linearly along the sequence, so a workgroup runs tile
   // p and tile n-1-p (equal total work) whenever that still leaves at least one workgroup per
   // compute unit; dQ from a dS bank takes query tiles of 256 rows, eight waves sharing each
-  // staged key tile.  Narrow windows: dK/dV key tiles of 64 rows (four waves, one LDS stage,
-  // two workgroups per CU), whose query range [c0, c0 + 64 + W - 1) wastes less of each
-  // 64-row query tile on the band's edges than 128-row key tiles do.
-  const bool wide = a.window >= 256 && a.window * 4 >= a.Skv;
+  // staged key tile.  Narrow windows (below 256): dK/dV key tiles of 64 rows (four waves, one
+  // LDS stage, two workgroups per CU), whose query range [c0, c0 + 64 + W - 1) wastes less of
+  // each 64-row query tile on the band's edges than 128-row key tiles do.  (Measured at S =
+  // 8192: equal at W = 256, the wide kernels 3 % faster at 512 and 11 % at 1024.)
+  const bool wide = a.window >= 256;
   const int bc = wide ? 128 : 64;
   const int nt = (a.Skv + bc - 1) / bc;
   AttnArgs ak = a, aq = a;

@@ -193,8 +193,8 @@ static long long ds_kb_of(int S, int window) {
 }
 static long long ds_blocks_of(int S, int window) { return ma::band_offset((S + 31) / 32, ds_kb_of(S, window)); }
 
-// Head split of the dK/dV work on dense wide windows (128-row key tiles, window >= 256 and
-// 4 window >= S) whose tiles cannot be paired (fewer than 256 pairs): one workgroup per key
+// Head split of the dK/dV work on dense wide windows (128-row key tiles, window >= 256) whose
+// tiles cannot be paired (fewer than 256 pairs): one workgroup per key
 // tile would leave the heaviest tile (the first, under a causal window) with about twice the
 // average work.  Each tile's visits (query heads x 64-row query tiles) are split over at most
 // `group` workgroups of whole heads, at most a quarter of a compute unit's share of all visits
@@ -206,7 +206,7 @@ struct WindowSplit {
 static WindowSplit window_split(int B, int Hq, int Hkv, int S, int window) {
   WindowSplit ws{0, 1};
   const int W = window < S ? window : S;
-  if (!(W >= 256 && (long long)W * 4 >= S)) return ws;
+  if (W < 256) return ws;
   const int nt = (S + 127) / 128;
   const long long units = (long long)B * Hkv;
   if (units * ((nt + 1) / 2) >= 256) return ws;

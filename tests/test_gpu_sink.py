@@ -110,11 +110,13 @@ def test_bwd_paired_tiles():
 # Dense wide windows with too few 128-row key tiles to pair: with the dS-bank workspace the
 # heaviest key tiles are split by query heads over several dK/dV workgroups (fp32 partials,
 # added in chunk order).  Splits of 3 chunks over 4 heads (uneven), a sliding window, two
-# sequences and a ragged last key tile.
+# sequences, a ragged last key tile, and a window far shorter than the sequence (one K/V head
+# shared by eight query heads).
 HEAD_SPLIT = [
     W.custom_sink("split_s600_causal", 1, 8, 2, 600, 600, torch.float16, seed_base=120),
     W.custom_sink("split_s700_w400_bf16", 1, 6, 2, 700, 400, torch.bfloat16, seed_base=121),
     W.custom_sink("split_b2_s1024_causal", 2, 8, 2, 1024, 1024, torch.float16, seed_base=122),
+    W.custom_sink("split_s2048_w300_mqa", 1, 8, 1, 2048, 300, torch.float16, seed_base=123),
 ]
 
 
