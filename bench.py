@@ -3,7 +3,7 @@
 
 Default workload: GQA sink attention backward, B=1 Hq=64 Hkv=8 S=8192 D=128, window = S
 (full causal), bf16 -- the dense-window configuration, the only one whose live tiles make
-it MFMA-bound.  One step = one whole backward call (preprocess + dsink reduce + dK/dV +
+it MFMA-bound.  One step = one whole backward call (preprocess + dK/dV with the dsink reduce +
 dQ; for block-sparse workloads also the table build) on inputs already resident in HBM.
 O and lse come from the library's own forward (untimed).
 

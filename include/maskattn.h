@@ -295,8 +295,9 @@ int attn_sink_bwd_varlen(const void* q, const void* k, const void* v,
  * and additionally record caller-created HIP events (hipEvent_t, passed as void*) on
  * `stream` between the stages, so per-stage device time can be read with
  * hipEventElapsedTime without a profiler:
- *   events[0] before the first kernel            events[1] after preprocess (+ dsink/tables)
- *   events[2] after the dK/dV kernel             events[3] after the dQ kernel
+ *   events[0] before the first kernel            events[1] after preprocess (+ tables)
+ *   events[2] after the dK/dV kernel (and the dsink reduce its first workgroup does, or the
+ *             block path's chunk reduce)         events[3] after the dQ kernel
  * events must point to 4 valid events (MA_EINVAL if events is NULL).
  * --------------------------------------------------------------------------------- */
 int attn_sink_bwd_timed(const void* q, const void* k, const void* v,

@@ -102,22 +102,6 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
   }
 }
 
-// dsink[h] = - sum_b sum_blk part[b,h,blk]: one wave per head, fixed order.
-__global__ __launch_bounds__(64) void dsink_reduce_kernel(const float* __restrict__ part, float* __restrict__ dsink,
-                                                          int B, int H, int nblk) {
-  const int h = blockIdx.x, lane = threadIdx.x;
-  float acc = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int i = lane; i < nblk; i += 64) acc += part[((size_t)b * H + h) * nblk + i];
-  acc += __shfl_xor(acc, 32);
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 8);
-  acc += __shfl_xor(acc, 4);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 1);
-  if (lane == 0) dsink[h] = -acc;
-}
-
 // Key blocks (block path) or key tiles (window path, head split) whose dK/dV sums span several
 // workgroups: sum the fp32 partials in chunk order (fixed, so results are bit-identical run to
 // run) and cast.  A 256-thread block covers 8 key rows x 128 columns (4 columns per thread) of
@@ -173,12 +157,6 @@ hipError_t launch_preprocess(int dtype, const void* o, const void* dout, const f
                              const int* cu, int total) {
   return dtype == 1 ? launch_preprocess_t<BF16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st, cu, total)
                     : launch_preprocess_t<F16>(o, dout, lse, sink, delta, lse2, part, B, H, S, st, cu, total);
-}
-
-hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, int S, hipStream_t st) {
-  const int nblk = (S + 63) / 64;
-  hipLaunchKernelGGL(dsink_reduce_kernel, dim3(H), dim3(64), 0, st, part, dsink, B, H, nblk);
-  return hipGetLastError();
 }
 
 hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid) {

@@ -700,6 +700,15 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
 template <class T, int MASK, int NK, bool DS = false>
 __global__ __launch_bounds__(2 * NK * 64, (dkdv_waves_per_simd<MASK, NK>())) void dkdv_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[DkdvShape<NK, dkdv_stages<MASK, NK>()>::smem_elems()];
+  if constexpr (MASK == MASK_WINDOW) {
+    // dsink of every query head (the preprocess that wrote the partials ran before this
+    // kernel), one wave per head in turn, before this workgroup's own tiles.
+    if (a.dsink_out != nullptr && blockIdx.x == 0) {
+      const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+      for (int h = w; h < a.Hq; h += 2 * NK)
+        dsink_head_sum(a.dsink_part, a.dsink_out, a.B, a.Hq, a.dsink_nblk, h, threadIdx.x & 63);
+    }
+  }
   const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   const int bh = wg % nbh, p = wg / nbh;

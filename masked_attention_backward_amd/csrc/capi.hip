@@ -259,10 +259,12 @@ static int sink_bwd_impl(const void* q, const void* k, const void* v, const void
   if (events) hipEventRecord((hipEvent_t)events[0], hs);
   hipError_t e = ma::launch_preprocess(dtype, o, dout, lse, sink, delta, lse2, part, B, Hq, S, hs, cu, total);
   if (e != hipSuccess) return MA_ELAUNCH;
-  e = ma::launch_dsink_reduce(part, dsink, B, Hq, S, hs);
-  if (e != hipSuccess) return MA_ELAUNCH;
   if (events) hipEventRecord((hipEvent_t)events[1], hs);
   AttnArgs a = base_args(q, k, v, B, Hq, Hkv, S, S, scale);
+  // dsink from the preprocess's partials, by the first dK/dV workgroup (no launch of its own).
+  a.dsink_part = part;
+  a.dsink_out = dsink;
+  a.dsink_nblk = (S + 63) / 64;
   a.dout = dout;
   a.lse = lse;
   a.lse2 = lse2;

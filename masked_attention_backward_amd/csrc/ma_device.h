@@ -217,7 +217,27 @@ struct AttnArgs {
   int dq_nw;             // window path with a dS bank: waves per dQ workgroup (4 or 8)
   int ds_nka;            // block path with a dS bank: 32-row key blocks per 32-row query block
                          // (bank entry of (head, qa, ka): head * ds_blocks + qa * ds_nka + ka)
+  const float* dsink_part;  // window path: the preprocess's dsink partials, [B][Hq][dsink_nblk]
+  float* dsink_out;         // window path: dsink [Hq], reduced by the first dK/dV workgroup
+                            // (nullptr: not reduced there)
+  int dsink_nblk;           // window path: partials per (sequence, head)
 };
+
+// dsink[h] = - sum_b sum_blk part[b][h][blk], by one wave: lane-strided partial sums in a
+// fixed order, then a butterfly over the 64 lanes (bit-identical run to run).
+__device__ __forceinline__ void dsink_head_sum(const float* __restrict__ part, float* __restrict__ dsink, int B,
+                                               int H, int nblk, int h, int lane) {
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int i = lane; i < nblk; i += 64) acc += part[((size_t)b * H + h) * nblk + i];
+  acc += __shfl_xor(acc, 32);
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (lane == 0) dsink[h] = -acc;
+}
 
 // Where the rows of sequence b lie in a tensor of H heads.  Dense: [B, H, S, D], S rows per
 // sequence.  Packed: [H, total, D] with sequence b at rows cu[b] .. cu[b + 1] of every head;

@@ -11,7 +11,6 @@ namespace ma {
 hipError_t launch_preprocess(int dtype, const void* o, const void* dout, const float* lse, const float* sink,
                              float* delta, float* lse2, float* part, int B, int H, int S, hipStream_t st,
                              const int* cu = nullptr, int total = 0);
-hipError_t launch_dsink_reduce(const float* part, float* dsink, int B, int H, int S, hipStream_t st);
 hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid = nullptr);
 hipError_t launch_block_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t ev_mid = nullptr);
 hipError_t launch_fwd(int dtype, AttnArgs a, int mask, hipStream_t st);
