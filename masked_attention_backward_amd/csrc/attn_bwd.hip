@@ -1,4 +1,4 @@
-// Host launchers of the attention backward: preprocess, dsink reduce, and the dispatch of
+// Host launchers of the attention backward: preprocess, the chunk reduce, and the dispatch of
 // the dK/dV and dQ kernels (their templates are in attn_bwd_kernels.h; each variant is
 // instantiated in its own object, see attn_bwd_variant.hip).
 #include "attn_bwd_kernels.h"
