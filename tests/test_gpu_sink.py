@@ -128,6 +128,35 @@ def test_bwd_head_split(wl):
     check_all(wl, x, ref)
 
 
+def random_sink_shapes(n=12, seed=20261203):
+    """Seeded random small shapes: batch 1-2, 1-4 K/V heads in groups of 1-4, lengths 1-700
+    (ragged tails), windows from 1 to past the sequence (narrow, wide, split and paired
+    launches), both dtypes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 5))
+        Hq = Hkv * int(rng.integers(1, 5))
+        S = int(rng.integers(1, 701))
+        win = int(rng.choice([1, int(rng.integers(1, 300)), int(rng.integers(256, 800)), S, S + 37]))
+        dt = torch.float16 if rng.integers(0, 2) == 0 else torch.bfloat16
+        out.append((B, Hq, Hkv, S, max(1, win), dt))
+    return out
+
+
+@pytest.mark.parametrize("shape", random_sink_shapes(), ids=lambda t: "B%d_Hq%d_Hkv%d_S%d_W%d_%s" % (
+    t[0], t[1], t[2], t[3], t[4], "f16" if t[5] == torch.float16 else "bf16"))
+def test_bwd_random_shapes(shape):
+    """Both dQ paths against the oracle, every element, on seeded random shapes."""
+    B, Hq, Hkv, S, win, dt = shape
+    wl = W.custom_sink("rand", B, Hq, Hkv, S, win, dt, seed_base=130 + S % 17)
+    x = with_oracle_forward(wl, W.make_inputs(wl))
+    ref = oracle.sink_attention_backward(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], x["sink"], wl.window,
+                                         wl.scale)
+    check_all(wl, x, ref)
+
+
 def test_head_split_deterministic_and_fully_written():
     """Head-split launch: three runs bit-identical; outputs and workspace (partials included)
     pre-filled with 0xFF are fully overwritten / never read before written."""
