@@ -166,7 +166,7 @@ def test_head_split_deterministic_and_fully_written():
     a = api()
     nbytes = a.attn_sink_bwd_ds_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.window)
     assert nbytes > a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq) + \
-        wl.B * wl.Hq * 2048 * ((wl.Sq + 31) // 32) * ((wl.Sq + 31) // 32 + 1) // 2   # partials present
+        wl.B * wl.Hq * 2048 * ((wl.Sq + 31) // 32) * ((wl.Sq + 31) // 32 + 1) // 2   # room for partials
     outs = []
     for _ in range(3):
         dq = torch.full_like(g["q"], float("nan"))
@@ -182,6 +182,12 @@ def test_head_split_deterministic_and_fully_written():
         assert st == 0
         torch.cuda.synchronize()
         outs.append([t.cpu() for t in (dq, dk, dv, dsink)])
+        # The split ran: the fp32 partials after the dS bank (causal window: the lower triangle
+        # of ceil(S/32) 32 x 32 blocks per head, 2 KiB each) were written.
+        nb = (wl.Sq + 31) // 32
+        part0 = a.attn_sink_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq) + \
+            (wl.B * wl.Hq * nb * (nb + 1) // 2 * 2048 + 255) // 256 * 256
+        assert bool((ws[part0:] != 0xFF).any())
     for t in outs[0]:
         assert torch.isfinite(t.float()).all()
     for other in outs[1:]:
