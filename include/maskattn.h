@@ -106,15 +106,16 @@ size_t attn_sink_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
  * query head): B * Hq * sum_a (min(a, kb) + 1) blocks, a over ceil(S/32) query blocks, kb =
  * ceil((min(window, S) - 1) / 32).  For window = S that is the lower triangle: 4.3 GB at
  * B = 1, Hq = 64, S = 8192.
- * Wide windows (W = min(window, S) >= 256) whose ceil(S/128) key tiles of 128
- * rows give B * Hkv * ceil(ceil(S/128) / 2) < 256 tile pairs: the bank is followed (at the
- * next 256-byte boundary) by the fp32 partial dK and dV of a head split of the dK/dV work,
- * 2 * B * Hkv * M * Sp * D * 4 bytes.  Key tile p's visits (its query heads times the 64-row
- * query tiles of rows [128 p, min(S, 128 p + 127 + W))) go to min(group, ceil(visits /
- * target)) workgroups of whole query heads, target = max(16, ceil(all tiles' visits * B *
- * Hkv / 1024)), M the largest such count (none when M = 1); the partial sums are added in
- * chunk order (deterministic).  268 MB at B = 1, Hq = 64, Hkv = 8, S = window = 4096 (M = 8;
- * the key tiles near the start see up to twice the average work).  Dense calls only: the
+ * When the key tiles give too few dK/dV workgroups to fill the GPU (W = min(window, S): W >=
+ * 256, key tiles of 128 rows, B * Hkv * ceil(ceil(S/128) / 2) < 256 tile pairs; W < 256, key
+ * tiles of 64 rows, B * Hkv * ceil(S/64) < 512), the bank is followed (at the next 256-byte
+ * boundary) by the fp32 partial dK and dV of a head split of the dK/dV work, 2 * B * Hkv * M *
+ * Sp * D * 4 bytes.  Key tile p's visits (its query heads times the 64-row query tiles of rows
+ * [bc p, min(S, bc p + bc - 1 + W)), bc the key tile rows) go to min(group, ceil(visits /
+ * target)) workgroups of whole query heads, target = max(1, ceil(all tiles' visits * B * Hkv /
+ * 1024)), M the largest such count (none when M = 1); the partial sums are added in chunk
+ * order (deterministic).  268 MB at B = 1, Hq = 64, Hkv = 8, S = window = 4096 (M = 8; the key
+ * tiles near the start see up to twice the average work).  Dense calls only: the
  * packed-sequence entry points do not split. */
 size_t attn_sink_bwd_ds_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int window);
 
@@ -276,7 +277,9 @@ int blocksparse_attn_bwd_gqa(const void* q, const void* k, const void* v,
  * written.  Errors as attn_sink_fwd / attn_sink_bwd, plus MA_EINVAL for a null or
  * misaligned cu_seqlens, total < 1, max_seqlen < 1 or max_seqlen > total.  With B equal
  * lengths S and a tensor relaid [B, H, S, D] -> [H, B*S, D] the results are attn_sink_fwd's
- * and attn_sink_bwd's.
+ * and attn_sink_bwd's, bit for bit wherever attn_sink_bwd does not split its key tiles by
+ * query heads (Hq = Hkv, or its minimum workspace); a split dense call sums dK and dV in
+ * another order (the packed entry points never split).
  * --------------------------------------------------------------------------------- */
 int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const float* sink,
                          const int* cu_seqlens, void* o, float* lse,

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void dkv_chunk_reduce_kernel(const AttnArgs a)
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int row = blockIdx.x * 8 + (threadIdx.x >> 5), col = (threadIdx.x & 31) * 4;
   if (row >= a.Skv) return;
-  const int nch = MASK == MASK_WINDOW ? window_chunks(a.Sq, a.window, a.group, a.chunk, row / 128)
+  const int nch = MASK == MASK_WINDOW ? window_chunks(a.Sq, a.window, a.group, a.chunk, row / window_key_rows(a.window))
                                       : block_chunks(a, b, kvh, row / a.by);
   if (nch <= 1) return;   // stored directly by its only workgroup
   const int skv_pad = (a.Skv + 63) & ~63;
@@ -168,7 +168,7 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   // LDS stage, two workgroups per CU), whose query range [c0, c0 + 64 + W - 1) wastes less of
   // each 64-row query tile on the band's edges than 128-row key tiles do.  (Measured at S =
   // 8192: equal at W = 256, the wide kernels 3 % faster at 512 and 11 % at 1024.)
-  const bool wide = a.window >= 256;
+  const bool wide = window_wide(a.window);
   const int bc = wide ? 128 : 64;
   const int nt = (a.Skv + bc - 1) / bc;
   AttnArgs ak = a, aq = a;
@@ -177,9 +177,9 @@ hipError_t launch_window_bwd(int dtype, AttnArgs a, hipStream_t st, hipEvent_t e
   aq.n_tiles = (a.Sq + 32 * aq.dq_nw - 1) / (32 * aq.dq_nw);
   const int pairs_dkdv = a.B * a.Hkv * ((nt + 1) / 2);
   const int pairs_dq = a.B * a.Hq * ((aq.n_tiles + 1) / 2);
-  // Head split (planned by the caller for dense wide windows whose tiles cannot be paired):
-  // max_chunks slots per key tile, the partial sums added by the chunk reduce.
-  const bool split = wide && !a.cu && a.max_chunks > 1;
+  // Head split (planned by the caller for dense sequences with too few key tiles to fill the
+  // GPU): max_chunks slots per key tile, the partial sums added by the chunk reduce.
+  const bool split = !a.cu && a.max_chunks > 1;
   if (!split) ak.max_chunks = 1;
   ak.pair = (!split && wide && pairs_dkdv >= 256) ? 1 : 0;
   aq.pair = (wide && pairs_dq >= 256) ? 1 : 0;

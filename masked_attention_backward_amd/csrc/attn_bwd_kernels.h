@@ -715,9 +715,9 @@ __global__ __launch_bounds__(2 * NK * 64, (dkdv_waves_per_simd<MASK, NK>())) voi
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   if constexpr (MASK == MASK_WINDOW) {
     constexpr int BC = 32 * NK;
-    if constexpr (NK == 4) {
+    {
       if (a.max_chunks > 1) {
-        // Head split (dense sequences, wide windows, too few tiles to pair): slot p holds chunk
+        // Head split (dense sequences, too few key tiles to fill the GPU): slot p holds chunk
         // max_chunks - 1 - p / n_tiles of key tile p % n_tiles, so the extra chunks of the
         // heaviest tiles are dispatched first; slots past a tile's chunk count return at once.
         const int kt = p % a.n_tiles, c = a.max_chunks - 1 - p / a.n_tiles;

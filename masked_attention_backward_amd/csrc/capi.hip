@@ -193,28 +193,31 @@ static long long ds_kb_of(int S, int window) {
 }
 static long long ds_blocks_of(int S, int window) { return ma::band_offset((S + 31) / 32, ds_kb_of(S, window)); }
 
-// Head split of the dK/dV work on dense wide windows (128-row key tiles, window >= 256) whose
-// tiles cannot be paired (fewer than 256 pairs): one workgroup per key
-// tile would leave the heaviest tile (the first, under a causal window) with about twice the
-// average work.  Each tile's visits (query heads x 64-row query tiles) are split over at most
-// `group` workgroups of whole heads, at most a quarter of a compute unit's share of all visits
-// each (at least 16; a half and an eighth measured slower on B1 H64 Hkv8 S4096); their fp32
-// partial sums are added in a fixed order.  max_chunks = 1: no split.
+// Head split of the dK/dV work on dense sequences whose key tiles give too few workgroups to
+// fill the GPU: wide windows (128-row key tiles) with fewer than 256 tile pairs, where one
+// workgroup per key tile would leave the heaviest tile (the first, under a causal window) with
+// about twice the average work; narrow windows (64-row key tiles, two workgroups per compute
+// unit) with fewer than 512 key tiles, whose few workgroups each walk a long chain of tiles
+// whose copies cannot be hidden.  Each tile's visits (query heads x 64-row query tiles) are
+// split over at most `group` workgroups of whole heads, at most a quarter of a compute unit's
+// share of all visits each (at least one visit; a half and an eighth measured no faster on
+// B1 H64 Hkv8 S4096); their fp32 partial sums are added in a fixed order.  max_chunks = 1: no
+// split.
 struct WindowSplit {
   int target, max_chunks;
 };
 static WindowSplit window_split(int B, int Hq, int Hkv, int S, int window) {
   WindowSplit ws{0, 1};
   const int W = window < S ? window : S;
-  if (W < 256) return ws;
-  const int nt = (S + 127) / 128;
+  const int bc = ma::window_key_rows(W);
+  const int nt = (S + bc - 1) / bc;
   const long long units = (long long)B * Hkv;
-  if (units * ((nt + 1) / 2) >= 256) return ws;
+  if (ma::window_wide(W) ? units * ((nt + 1) / 2) >= 256 : units * nt >= 512) return ws;
   const int group = Hq / Hkv;
   long long visits = 0;
   for (int p = 0; p < nt; ++p) visits += (long long)group * ma::window_qtiles(S, W, p);
   const long long t = (units * visits + 1023) / 1024;
-  ws.target = (int)(t < 16 ? 16 : t > (1ll << 30) ? (1ll << 30) : t);
+  ws.target = (int)(t < 1 ? 1 : t > (1ll << 30) ? (1ll << 30) : t);
   for (int p = 0; p < nt; ++p) {
     const int c = ma::window_chunks(S, W, group, ws.target, p);
     if (c > ws.max_chunks) ws.max_chunks = c;

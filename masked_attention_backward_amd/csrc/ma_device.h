@@ -272,16 +272,21 @@ __device__ __host__ __forceinline__ long long band_offset(long long a, long long
   // sum over a' < a of (min(a', kb) + 1)
   return a <= kb + 1 ? a * (a + 1) / 2 : (kb + 1) * (kb + 2) / 2 + (a - kb - 1) * (kb + 1);
 }
-// Window path, wide windows (128-row key tiles): the 64-row query tiles key tile p visits
-// (rows [128 p, min(S, 128 p + 128 + W - 1)) of every query head of its group).
+// Window path: windows of at least 256 tokens take the eight-wave dK/dV kernel over 128-row
+// key tiles, shorter ones the four-wave kernel over 64-row key tiles (W = min(window, S)).
+__device__ __host__ __forceinline__ bool window_wide(int W) { return W >= 256; }
+__device__ __host__ __forceinline__ int window_key_rows(int W) { return window_wide(W) ? 128 : 64; }
+// The 64-row query tiles key tile p visits: rows [c0, min(S, c0 + bc + W - 1)) of every query
+// head of its group, c0 = bc p, bc = window_key_rows(W).
 __device__ __host__ __forceinline__ int window_qtiles(int S, int W, int p) {
-  const int c0 = p * 128;
-  const int qend = S < c0 + 128 + W - 1 ? S : c0 + 128 + W - 1;
+  const int bc = window_key_rows(W);
+  const int c0 = p * bc;
+  const int qend = S < c0 + bc + W - 1 ? S : c0 + bc + W - 1;
   const int n = ((qend + 63) >> 6) - (c0 >> 6);
   return n > 0 ? n : 0;
 }
-// Head split of wide-window key tiles that cannot be paired: the workgroups key tile p's
-// visits (query heads x query tiles) are spread over, whole query heads each, at most
+// Head split of key tiles when too few workgroups would fill the GPU: the workgroups key tile
+// p's visits (query heads x query tiles) are spread over, whole query heads each, at most
 // `target` visits per workgroup where the group allows (1: not split).
 __device__ __host__ __forceinline__ int window_chunks(int S, int W, int group, int target, int p) {
   const int n = (group * window_qtiles(S, W, p) + target - 1) / target;

@@ -108,7 +108,8 @@ def brute_band_blocks(S, W):
 
 def test_ds_workspace_query(lib):
     """The dS-bank workspace: the minimum one plus 2048 bytes per live 32 x 32 block of every
-    (batch, query head), the block count checked against a brute-force scan of the band."""
+    (batch, query head), the block count checked against a brute-force scan of the band (plus
+    the head split's partial sums where it applies, see test_ds_workspace_head_split)."""
     Z, I = ctypes.c_size_t, ctypes.c_int
     lib.attn_sink_bwd_workspace_bytes.restype = Z
     lib.attn_sink_bwd_ds_workspace_bytes.restype = Z
@@ -118,7 +119,9 @@ def test_ds_workspace_query(lib):
         base = lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, 128)
         full = lib.attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, 128, W)
         bank = B * Hq * brute_band_blocks(S, min(W, S)) * 2048
-        assert full == base + (bank + 255) // 256 * 256, (B, Hq, S, W)
+        mc = split_plan(B, Hq, Hkv, S, W)
+        part = 0 if mc == 1 else -(-2 * B * Hkv * mc * (-(-S // 64) * 64) * 128 * 4 // 256) * 256
+        assert full == base + (bank + 255) // 256 * 256 + part, (B, Hq, S, W)
     assert lib.attn_sink_bwd_ds_workspace_bytes(1, 64, 8, 8192, 128, 8192) == \
         lib.attn_sink_bwd_workspace_bytes(1, 64, 8, 8192, 128) + 64 * (256 * 257 // 2) * 2048
     assert lib.attn_sink_bwd_ds_workspace_bytes(1, 4, 1, 128, 128, 0) == 0
@@ -126,17 +129,18 @@ def test_ds_workspace_query(lib):
 
 
 def split_plan(B, Hq, Hkv, S, window):
-    """The head split of wide-window key tiles, derived from its stated rule: dense wide windows
-    (W >= 256) whose 128-row key tiles give fewer than 256 pairs; a key tile's visits
-    (query heads x 64-row query tiles of rows [128 p, min(S, 128 p + 127 + W))) split over at
-    most group workgroups of about max(16, ceil(all visits / 1024)) visits each."""
+    """The head split of key tiles, derived from its stated rule: dense windows whose key tiles
+    (128 rows for W >= 256, else 64) give fewer than 256 pairs (wide) or 512 tiles (narrow); a
+    key tile's visits (query heads x 64-row query tiles of rows [bc p, min(S, bc p + bc - 1 +
+    W))) split over at most group workgroups of about max(1, ceil(all visits / 1024)) each."""
     W = min(window, S)
-    nt = -(-S // 128)
-    if W < 256 or B * Hkv * -(-nt // 2) >= 256:
+    bc = 128 if W >= 256 else 64
+    nt = -(-S // bc)
+    if (W >= 256 and B * Hkv * -(-nt // 2) >= 256) or (W < 256 and B * Hkv * nt >= 512):
         return 1
     g = Hq // Hkv
-    qt = [len(range(128 * p // 64, -(-min(S, 128 * p + 127 + W) // 64))) for p in range(nt)]
-    target = max(16, -(-B * Hkv * g * sum(qt) // 1024))
+    qt = [len(range(bc * p // 64, -(-min(S, bc * p + bc - 1 + W) // 64))) for p in range(nt)]
+    target = max(1, -(-B * Hkv * g * sum(qt) // 1024))
     return max(min(g, max(1, -(-g * n // target))) for n in qt)
 
 
@@ -149,7 +153,8 @@ def test_ds_workspace_head_split(lib):
     lib.attn_sink_bwd_ds_workspace_bytes.argtypes = [I] * 6
     seen_split = 0
     for B, Hq, Hkv, S, W in [(1, 64, 8, 4096, 4096), (1, 8, 2, 600, 600), (1, 6, 2, 700, 400), (2, 8, 2, 1024, 1024),
-                             (1, 4, 4, 520, 300), (1, 64, 8, 8192, 8192), (1, 8, 1, 2048, 300), (4, 16, 16, 1024, 1024)]:
+                             (1, 4, 4, 520, 300), (1, 64, 8, 8192, 8192), (1, 8, 1, 2048, 300), (4, 16, 16, 1024, 1024),
+                             (1, 4, 1, 128, 64), (2, 32, 8, 2048, 128), (1, 8, 1, 2048, 2048), (3, 6, 3, 77, 5)]:
         base = lib.attn_sink_bwd_workspace_bytes(B, Hq, Hkv, S, 128)
         bank = -(-B * Hq * brute_band_blocks(S, min(W, S)) * 2048 // 256) * 256
         mc = split_plan(B, Hq, Hkv, S, W)
@@ -157,7 +162,8 @@ def test_ds_workspace_head_split(lib):
         seen_split += mc > 1
         assert lib.attn_sink_bwd_ds_workspace_bytes(B, Hq, Hkv, S, 128, W) == base + bank + part, (B, Hq, Hkv, S, W)
     assert split_plan(1, 64, 8, 4096, 4096) == 8 and split_plan(1, 64, 8, 8192, 8192) == 1
-    assert seen_split == 5
+    assert split_plan(1, 4, 1, 128, 64) == 4 and split_plan(2, 32, 8, 2048, 128) == 1
+    assert seen_split == 8
 
 
 def test_block_ds_workspace_query(lib):

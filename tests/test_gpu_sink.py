@@ -107,16 +107,18 @@ def test_bwd_paired_tiles():
     check_all(wl, x, ref, delta=False)
 
 
-# Dense wide windows with too few 128-row key tiles to pair: with the dS-bank workspace the
-# heaviest key tiles are split by query heads over several dK/dV workgroups (fp32 partials,
-# added in chunk order).  Splits of 3 chunks over 4 heads (uneven), a sliding window, two
-# sequences, a ragged last key tile, and a window far shorter than the sequence (one K/V head
-# shared by eight query heads).
+# Dense windows with too few key tiles to fill the GPU: with the dS-bank workspace key tiles
+# are split by query heads over several dK/dV workgroups (fp32 partials, added in chunk
+# order).  A sliding window, two sequences, a ragged last key tile, a window far shorter than
+# the sequence, and one K/V head shared by eight query heads under a causal window, whose last
+# key tiles split into 6 chunks over 8 heads (uneven); the small narrow-window shapes of the
+# other tests split too.
 HEAD_SPLIT = [
     W.custom_sink("split_s600_causal", 1, 8, 2, 600, 600, torch.float16, seed_base=120),
     W.custom_sink("split_s700_w400_bf16", 1, 6, 2, 700, 400, torch.bfloat16, seed_base=121),
     W.custom_sink("split_b2_s1024_causal", 2, 8, 2, 1024, 1024, torch.float16, seed_base=122),
     W.custom_sink("split_s2048_w300_mqa", 1, 8, 1, 2048, 300, torch.float16, seed_base=123),
+    W.custom_sink("split_s2048_causal_mqa_bf16", 1, 8, 1, 2048, 2048, torch.bfloat16, seed_base=124),
 ]
 
 

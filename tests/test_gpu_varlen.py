@@ -91,22 +91,29 @@ def test_fwd_small(case):
     check("lse", lse, lse_ref, dtype)
 
 
-def test_equal_lengths_bit_identical_to_dense():
+@pytest.mark.parametrize("hq,hkv,path", [(2, 2, "ds_bank"), (4, 2, "recompute")], ids=["mha_bank", "gqa_recompute"])
+def test_equal_lengths_bit_identical_to_dense(hq, hkv, path):
     """B sequences of one length S are the dense [B, H, S, D] call relaid to [H, B*S, D]: the
-    same tiles in the same order, so every output is bit-identical."""
-    B, S, hq, hkv, window, dtype = 3, 200, 4, 2, 90, torch.float16
+    same tiles in the same order, so every output is bit-identical, wherever the dense call
+    does not split its key tiles by query heads (one query head per K/V head, or the minimum
+    workspace; a split dense call sums dK/dV in another order and agrees to rounding)."""
+    B, S, window, dtype = 3, 200, 90, torch.float16
     x = with_oracle_forward(W.varlen_inputs([S] * B, hq, hkv, dtype, seed_base=406), window, dtype)
-    dq, dk, dv, dsink = gpu_bwd("equal_lengths", x, window)
+    dq, dk, dv, dsink = gpu_bwd("equal_lengths", x, window, path)
 
     def dense(t):   # [H, B*S, ...] -> [B, H, S, ...]
         return t.reshape(t.shape[0], B, S, *t.shape[2:]).transpose(0, 1).contiguous().to(DEV)
 
-    print("[gpu] attn_sink_bwd dense twin", flush=True)
-    r = api().attn_sink_bwd(dense(x["q"]), dense(x["k"]), dense(x["v"]), dense(x["o"]), dense(x["do"]),
-                            dense(x["lse"]), x["sink"].to(DEV), window, SCALE)
-    fo, flse = api().attn_sink_fwd_varlen(*(x[n].to(DEV) for n in ("q", "k", "v", "sink", "cu_seqlens")), S,
-                                          window, SCALE)
-    ro, rlse = api().attn_sink_fwd(dense(x["q"]), dense(x["k"]), dense(x["v"]), x["sink"].to(DEV), window, SCALE)
+    print(f"[gpu] attn_sink_bwd dense twin ({path})", flush=True)
+    a = api()
+    ws = None
+    if path == "recompute":
+        ws = torch.empty(a.attn_sink_bwd_workspace_bytes(B, hq, hkv, S), dtype=torch.uint8, device=DEV)
+    r = a.attn_sink_bwd(dense(x["q"]), dense(x["k"]), dense(x["v"]), dense(x["o"]), dense(x["do"]),
+                        dense(x["lse"]), x["sink"].to(DEV), window, SCALE, workspace=ws)
+    fo, flse = a.attn_sink_fwd_varlen(*(x[n].to(DEV) for n in ("q", "k", "v", "sink", "cu_seqlens")), S,
+                                      window, SCALE)
+    ro, rlse = a.attn_sink_fwd(dense(x["q"]), dense(x["k"]), dense(x["v"]), x["sink"].to(DEV), window, SCALE)
     torch.cuda.synchronize()
     for got, want in ((dq, r[0]), (dk, r[1]), (dv, r[2]), (fo, ro), (flse, rlse)):
         assert torch.equal(dense(got.cpu()), want)
