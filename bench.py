@@ -170,7 +170,7 @@ class HipEvents:
 
 def blas_threads():
     """Threads the oracle's BLAS may use: the CPUs this process may run on, capped by
-    OMP_NUM_THREADS when that is set (the GPU machine's CPU share)."""
+    OMP_NUM_THREADS when that is set (the host's CPU share for this process)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit() and int(env) > 0:

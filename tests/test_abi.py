@@ -25,7 +25,7 @@ def declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libmaskattn.so is not built (run __graft_entry__.build())")
+        pytest.fail("libmaskattn.so is not built (run python -m masked_attention_backward_amd.build)")
     return ctypes.CDLL(LIB)
 
 
