@@ -134,18 +134,14 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
         }
       }
     }
-    // Scaled logits in the log2 domain.
+    // Running max in the log2 domain: the largest raw logit times the (positive) scale, which
+    // rounds to the same value as the largest scaled logit.
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = s[mb][r] * sl2;
-        s[mb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     const float mnew = fmaxf(m2, mx);
     const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
     float rs = 0.f;
@@ -153,19 +149,24 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // A finite logit implies a finite running max no smaller than it.
-        const float p = (s[mb][r] == -INFINITY) ? 0.f : fast_exp2(s[mb][r] - mnew);
+        // P = exp2(s scale - m), one fused multiply-add per logit; a finite logit implies a
+        // finite running max no smaller than it.
+        const float p = (s[mb][r] == -INFINITY) ? 0.f : fast_exp2(fmaf(s[mb][r], sl2, -mnew));
         s[mb][r] = p;
         rs += p;
       }
     }
     rs += __shfl_xor(rs, 32);
     l = l * alpha + rs;
+    // The accumulators are rescaled only when some row's max grew (alpha = 1 exactly
+    // otherwise; the test is a ballot, uniform over the wave).
+    if (__builtin_amdgcn_ballot_w64(mnew != m2) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
+    }
     m2 = mnew;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const u32x4 pb = pack8<T>(s[t4 >> 1], 8 * (t4 & 1));
