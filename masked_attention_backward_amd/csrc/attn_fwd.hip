@@ -144,14 +144,16 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, int b, int hq, int r
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     const float mnew = fmaxf(m2, mx);
     const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+    // P = exp2(s scale - m), one fused multiply-add per logit.  A hidden logit (-inf) gives
+    // exp2(-inf) = 0 exactly; a row whose max is still -inf has only hidden logits, and takes 0
+    // as its offset so that no -inf - -inf arises.
+    const float msub = (mnew == -INFINITY) ? 0.f : mnew;
     float rs = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // P = exp2(s scale - m), one fused multiply-add per logit; a finite logit implies a
-        // finite running max no smaller than it.
-        const float p = (s[mb][r] == -INFINITY) ? 0.f : fast_exp2(fmaf(s[mb][r], sl2, -mnew));
+        const float p = fast_exp2(fmaf(s[mb][r], sl2, -msub));
         s[mb][r] = p;
         rs += p;
       }
