@@ -202,16 +202,21 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
 size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by);
 
 /* Workspace that also holds the block path's dS bank: blocksparse_attn_bwd_workspace_bytes()
- * plus, when bx and by are multiples of 32 (and a head's grid of 32 x 32 blocks has fewer than
- * 2^30 entries), 2048 bytes per (query head, 32-row query block, 32-row key block) of the dense
- * grid: B * N * ceil(Sq/32) * ceil(Skv/32) * 2048 bytes at the end of the workspace (256-byte
- * aligned).  Otherwise equal to blocksparse_attn_bwd_workspace_bytes().  Passing at least
- * this many bytes to blocksparse_attn_bwd(_gqa) makes the dK/dV kernel store the 16-bit dS of
- * every selected 32 x 32 block and the dQ kernel read it back, one GEMM per block, instead
- * of recomputing S and dP: the second pass of the five-GEMM scheme of the block-sparse page's
- * handbook ("single-pass 5-dot fusion + partial workspace + reduce"), with dS rather than fp32
- * dQ partials as the intermediate.  Results are deterministic either way (fixed key order).
- * Only entries inside selected mask blocks are written or read. */
+ * plus 2048 bytes per entry of a grid of 32 x 32 blocks of every (batch, query head): 32-row
+ * query blocks (rows 32 i ..) by nka key sub-blocks, where nka = ceil(Skv/32) when by is a
+ * multiple of 32 (the dense 32-row key grid) and ceil(Skv/by) * ceil(by/32) otherwise (the
+ * sub-blocks of 32 rows starting at each mask block's first key row, the last one of a block
+ * partly past it):  B * N * ceil(Sq/32) * nka * 2048 bytes at the end of the workspace
+ * (256-byte aligned), provided a head's grid has fewer than 2^30 entries; otherwise equal to
+ * blocksparse_attn_bwd_workspace_bytes().  Passing at least this many bytes to
+ * blocksparse_attn_bwd(_gqa) makes the dK/dV kernel store the 16-bit dS of every 32 x 32 block
+ * holding a selected (query, key) pair and the dQ kernel read it back, one GEMM per block,
+ * instead of recomputing S and dP: the second pass of the five-GEMM scheme that the
+ * block-sparse page's handbook lists among its next optimisations (a single pass computing the
+ * five products, partial sums in a workspace, then a reduce), with dS rather than fp32 dQ
+ * partials as the intermediate.  Rows and key columns of an entry outside the selected mask
+ * blocks hold exact zeros.  Results are deterministic either way (fixed key order).  Only
+ * entries touching selected mask blocks are written or read. */
 size_t blocksparse_attn_bwd_ds_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by);
 
 /* ---------------------------------------------------------------------------------

@@ -217,6 +217,12 @@ static void launch_block_t(const AttnArgs& a, hipStream_t st, hipEvent_t ev_mid)
     hipLaunchKernelGGL((dkv_chunk_reduce_kernel<T, MASK_BLOCK>), dim3((a.Skv + 7) / 8, a.Hkv, a.B), dim3(256), 0,
                        st, a);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
+  if (a.ds_bank && (a.bx % 32 != 0 || a.by % 32 != 0)) {
+    // dS bank with query halves or key sub-blocks off the 32-row grid: one wave per 32-row
+    // query half, four per workgroup.
+    hipLaunchKernelGGL(dq_ds_blocku_kernel<T>, dim3(a.B * a.Hq * ((a.Sq + 127) / 128)), dim3(256), 0, st, a);
+    return;
+  }
   switch (nwq) {
     case 1: launch_dq_variant<T, MASK_BLOCK, 1>(a, gq, st); break;
     case 2: launch_dq_variant<T, MASK_BLOCK, 2>(a, gq, st); break;

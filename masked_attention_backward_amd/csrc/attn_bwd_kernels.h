@@ -150,6 +150,31 @@ __device__ __forceinline__ int block_chunks(const AttnArgs& a, int b, int kvh, i
   return max(1, (e + a.chunk - 1) / a.chunk);
 }
 
+// Query blocks whose size is not a multiple of 32 rows: two selected blocks of one head can
+// share a 32-row query half, whose dS bank entry the dK/dV workgroup visiting that half stores
+// once with the rows of both.  A chunk boundary between two such blocks would have two
+// workgroups store that entry, each with only its own rows, so a boundary x (an index into the
+// key block's concatenated table rows; x >= the entry count is returned as is) moves past every
+// entry that shares a half with the entry before it in the same head.  Both neighbouring chunks
+// compute the same boundary, so the chunks still cover every entry exactly once.
+__device__ __forceinline__ int block_chunk_edge(const AttnArgs& a, int b, int kvh, int kblock, int x) {
+  const size_t row0 = ((size_t)b * a.Hq + (size_t)kvh * a.group) * a.nkb + kblock;
+  const_int_ptr cnt = (const_int_ptr)a.cnt_k;
+  int base = 0;
+  for (int h = 0; h < a.group; ++h) {
+    const size_t row = row0 + (size_t)h * a.nkb;
+    const int n = cnt[row];
+    if (x < base + n) {
+      const_int_ptr sel = (const_int_ptr)a.sel_k + row * a.nqb;
+      int i = x - base;
+      while (i > 0 && i < n && (min(sel[i - 1] * a.bx + a.bx, a.Sq) - 1) >> 5 == (sel[i] * a.bx) >> 5) ++i;
+      return base + i;
+    }
+    base += n;
+  }
+  return x;
+}
+
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (B < E) {
@@ -291,8 +316,16 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
     // A head split takes query heads hoff .. hoff + hcnt - 1 of the group only.
     wsrc = WindowSourceDesc::make(kvh * a.group + hoff, hcnt > 0 ? hcnt : a.group, tlo, max(0, thi - tlo), NK <= 2);
   } else {
-    if (a.chunk > 0) bsrc.init(a, b, kvh, kblock, chunk * a.chunk, a.chunk);
-    else bsrc.init(a, b, kvh, kblock, 0, 0x7fffffff);
+    if (a.chunk > 0) {
+      int first = chunk * a.chunk, count = a.chunk;
+      if (DS && (a.bx & 31) != 0) {
+        first = block_chunk_edge(a, b, kvh, kblock, first);
+        count = block_chunk_edge(a, b, kvh, kblock, (chunk + 1) * a.chunk) - first;
+      }
+      bsrc.init(a, b, kvh, kblock, first, count);
+    } else {
+      bsrc.init(a, b, kvh, kblock, 0, 0x7fffffff);
+    }
   }
   auto fetch = [&](TileRef& r) -> bool {
     if constexpr (MASK == MASK_WINDOW) return wsrc.next(r.head, r.tile, r.bits);
@@ -506,12 +539,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnArgs& a, int b, int kvh, int
       bool ds_edge = false;   // wave-uniform: the block reaches past the last key row
       u32x4* ds_dst = nullptr;
       if constexpr (MASK == MASK_BLOCK && DS) {
-        // Block path (block sizes multiples of 32, so this wave's 32 x 32 block lies inside one
-        // mask block): entry (head, qa, ka) of the dense grid, stored when some of its query
-        // rows are selected; key columns past the last key row are stored as zeros.
-        const int qa = 2 * cur.tile + qh, ka = (c0 >> 5) + kb;
-        ds_live = ((cur.bits >> (32 * qh)) & 0xffffffffull) != 0 && ka * 32 < kv_end;
-        ds_edge = ka * 32 + 32 > kv_end;
+        // Block path: entry (head, qa, ka) of the grid of 32-row query halves and key
+        // sub-blocks, ka = kblock NK + kb (the 32 key rows c0 + 32 kb .. of this mask block's
+        // workgroup; the global 32-row key block when by is a multiple of 32), stored when some
+        // of its query rows are selected (unselected rows hold exact zeros); key columns past
+        // the block's last row (the next block's, or past the end) are stored as zeros.
+        const int qa = 2 * cur.tile + qh, ka = kblock * NK + kb;
+        ds_live = ((cur.bits >> (32 * qh)) & 0xffffffffull) != 0 && c0 + 32 * kb < kv_end;
+        ds_edge = c0 + 32 * kb + 32 > kv_end;
         const long long blk = ((long long)b * a.Hq + cur.head) * a.ds_blocks + (qa * a.ds_nka + ka);
         ds_dst = reinterpret_cast<u32x4*>(a.ds_bank + (ds_live ? blk : 0) * 1024) + lane;
       }
@@ -1265,6 +1300,150 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_ds_block_kernel(const AttnArgs 
 
 // Launch of one (element type, mask kind, NW) variant: dK/dV with 2 NW waves (NW key blocks
 // of 32 rows), dQ with NW waves (NW query blocks of 32 rows).
+// Block path with a dS bank when bx or by is not a multiple of 32 (the dK/dV kernel's 32-row
+// query halves then straddle query blocks, and its key sub-blocks c0 + 32 kb are off the
+// 32-row grid).  Every wave owns one 32-row query half qa (rows 32 qa ..) and works alone:
+// it walks, in ascending order, the union of the key blocks selected by the (at most three)
+// query blocks its rows fall in, and for each key block the sub-blocks that hold key rows,
+// one GEMM per sub-block from its dS bank entry (qa, kb NK + j).  The entry exists exactly
+// when one of those query blocks selects kb (the dK/dV kernel stored it then), and its rows
+// of query blocks that do not select kb are exact zeros.  Key rows and dS blocks go through
+// the wave's own two LDS buffers (one sub-block ahead, LDS DMA, vmcnt waits only: no
+// barriers), so waves of one workgroup never wait for each other.
+constexpr int DQU_BUF_BYTES = 8192 + 2048;          // 32 key rows, one 32 x 32 dS block
+constexpr int DQU_WAVE_BYTES = 2 * DQU_BUF_BYTES;    // two buffers per wave (20 KiB)
+static_assert(DQU_WAVE_BYTES >= EPI_ELEMS * 2, "the epilogue stages through the wave's buffers");
+
+template <class T>
+__device__ __forceinline__ void dq_ds_blocku_wave(const AttnArgs& a, int b, int hq, int qa, uint16_t* buf,
+                                                  int lane) {
+  const int h = lane >> 5;
+  const SeqRows qs = seq_rows(a, b, a.Hq, a.Sq), ks = seq_rows(a, b, a.Hkv, a.Skv);
+  const int sq = qs.len, skv = ks.len;
+  const int q0 = qa * 32;
+  if (q0 >= sq) return;   // wave-uniform; no barriers follow
+  const uint32_t buf_lds = __builtin_amdgcn_readfirstlane(lds_addr(buf));
+  const size_t qrow0 = qs.base + (size_t)hq * qs.head_stride;
+  const int kvh = hq / a.group;
+  const uint16_t* Kp = (const uint16_t*)a.k + (ks.base + (size_t)kvh * ks.head_stride) * HD;
+  const uint16_t* bank =
+      a.ds_bank + (((long long)b * a.Hq + hq) * a.ds_blocks + (long long)qa * a.ds_nka) * 1024;
+  const int nks = (a.by + 31) >> 5;   // key sub-blocks per mask block
+
+  // The query blocks of rows [q0, min(q0 + 32, sq)): at most three (bx >= 16).
+  const size_t qhead = (size_t)b * a.Hq + hq;
+  const int qb0 = q0 / a.bx, qb1 = min(a.nqb - 1, (min(q0 + 32, sq) - 1) / a.bx);
+  const_int_ptr sel[3];
+  int cnt[3], pos[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int qb = min(qb0 + i, qb1);
+    sel[i] = (const_int_ptr)a.sel_q + (qhead * a.nqb + qb) * a.nkb;
+    cnt[i] = qb0 + i <= qb1 ? ((const_int_ptr)a.cnt_q)[qhead * a.nqb + qb] : 0;
+  }
+  // Next key block of the union (ascending; -1 when done).
+  auto next_kb = [&]() -> int {
+    int m = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (pos[i] < cnt[i]) m = min(m, sel[i][pos[i]]);
+    if (m == 0x7fffffff) return -1;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (pos[i] < cnt[i] && sel[i][pos[i]] == m) ++pos[i];
+    return m;
+  };
+  // The sub-block after (kb, j): the next one of kb that holds key rows, else the next key block.
+  auto advance = [&](int& kb, int& j) {
+    ++j;
+    if (j >= nks || kb * a.by + 32 * j >= min(kb * a.by + a.by, skv)) {
+      kb = next_kb();
+      j = 0;
+    }
+  };
+
+  auto src_chunk = [&](int u) -> uint32_t {
+    const int m = 2 * (lane >> 4) + (((lane >> 3) & 1) ^ u);
+    return (uint32_t)(u * 1024 + (32 * ((lane >> 2) & 1) + 4 * m + (lane & 3)) * 16);
+  };
+  const uint32_t so0 = src_chunk(0), so1 = src_chunk(1);
+  const int g = (lane >> 4) & 1, ia = lane & 3, ir = (lane >> 2) & 3;
+  const int dso = g * 1024 + 128 * (g ^ h) + 64 * (ia & 1) + 16 * ir + 8 * (ia >> 1);
+  // Key rows of a sub-block: unit u (four rows) per instruction, row 4 u + lane / 16 of the 32,
+  // the swizzle of a staged tile's first 32 rows, rows past the end clamped (their dS is 0).
+  uint32_t kcol[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 4 * u + (lane >> 4);
+    kcol[u] = (uint32_t)((((lane & 15) ^ swz(row)) << 3));
+  }
+  auto issue = [&](int kb, int j, int s) {
+    const int row0 = kb * a.by + 32 * j;
+    const uint32_t d = buf_lds + (uint32_t)(s * DQU_BUF_BYTES);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int gr = min(row0 + 4 * u + (lane >> 4), skv - 1);
+      dma16(Kp, 2u * ((uint32_t)gr * HD + kcol[u]), __builtin_amdgcn_readfirstlane(d + (uint32_t)(u * 1024)));
+    }
+    const uint16_t* blk = bank + (long long)(kb * nks + j) * 1024;
+    dma16nt(blk, so0, __builtin_amdgcn_readfirstlane(d + 8192u));
+    dma16nt(blk, so1, __builtin_amdgcn_readfirstlane(d + 9216u));
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = zero16();
+  FragOff fo(lane);
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  auto ds_frag = [&](const char* blk, int tt) -> u32x4 {
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt + 256));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    return (u32x4){xa[0], xa[1], ya[0], ya[1]};
+  };
+
+  int kb = next_kb(), j = 0, s = 0;
+  if (kb >= 0) issue(kb, j, 0);
+  while (kb >= 0) {
+    int nk = kb, nj = j;
+    advance(nk, nj);
+    if (nk >= 0) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the other buffer done
+      issue(nk, nj, s ^ 1);
+      wait_vmcnt<10>();   // this sub-block's ten copies landed; the next one's may fly
+    } else {
+      wait_vmcnt<0>();
+    }
+    const uint16_t* kt = buf + s * (DQU_BUF_BYTES / 2);
+    const char* dsb = reinterpret_cast<const char*>(buf) + s * DQU_BUF_BYTES + 8192;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const u32x4 fa = ds_frag(dsb, tt);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa, frag_col(kt, fo, 0, tt, nb), acc[nb]);
+    }
+    kb = nk;
+    j = nj;
+    s ^= 1;
+  }
+  // Epilogue through the wave's own buffers (every copy landed, every read done).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  store_tile_rows<T>(acc, a.scale, (uint16_t*)a.dq + (qrow0 + q0) * HD, min(32, sq - q0), buf, lane);
+}
+
+template <class T>
+__global__ __launch_bounds__(4 * 64, 2) void dq_ds_blocku_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * DQU_WAVE_BYTES / 2];
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  // Four 32-row halves per workgroup.  Workgroups of one (batch, head) are consecutive modulo
+  // B Hq, so with B Hq a multiple of 8 each lands on the XCD that holds its head's K rows and
+  // bank blocks in L2.
+  const int nbh = a.B * a.Hq;
+  const int bh = blockIdx.x % nbh, t = blockIdx.x / nbh;
+  dq_ds_blocku_wave<T>(a, bh / a.Hq, bh % a.Hq, 4 * t + w, smem + w * (DQU_WAVE_BYTES / 2), lane);
+}
+
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.ds_bank) {

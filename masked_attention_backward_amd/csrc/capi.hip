@@ -392,18 +392,23 @@ size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D
   return block_layout(B, N, Sq, Skv, nqb, nkb).total;
 }
 
-// dS bank of the block path (block sizes that are multiples of 32, so the dK/dV and dQ kernels
-// tile queries and keys on the same 32-row grid): one 2048-byte entry per (query head, 32-row
-// query block, 32-row key block) of the dense grid; only entries inside selected mask blocks
-// are written and read.  Kept below 2^30 entries per head (32-bit offsets in the kernels).
+// dS bank of the block path: one 2048-byte entry per (query head, 32-row query half, key
+// sub-block) of a dense grid, key sub-block kb ceil(by/32) + j holding key rows kb by + 32 j ..
+// of mask block kb (when by is a multiple of 32 that is the global 32-row key block, and the
+// grid has ceil(Skv/32) of them; otherwise nkb ceil(by/32)); only entries inside selected
+// mask blocks are written and read.  Kept below 2^30 entries per head (32-bit offsets in the
+// kernels).
+static long long block_bank_nka(int Skv, int by) {
+  return by % 32 == 0 ? (Skv + 31) / 32 : (long long)((Skv + by - 1) / by) * ((by + 31) / 32);
+}
 static bool block_bank_ok(int Sq, int Skv, int bx, int by) {
-  return bx % 32 == 0 && by % 32 == 0 && (long long)((Sq + 31) / 32) * ((Skv + 31) / 32) < (1ll << 30);
+  return bx % 16 == 0 && by % 16 == 0 && (long long)((Sq + 31) / 32) * block_bank_nka(Skv, by) < (1ll << 30);
 }
 
 size_t blocksparse_attn_bwd_ds_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by) {
   const size_t base = blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, D, bx, by);
   if (base == 0 || !block_bank_ok(Sq, Skv, bx, by)) return base;
-  return base + align256((size_t)B * N * (size_t)((Sq + 31) / 32) * (size_t)((Skv + 31) / 32) * 2048);
+  return base + align256((size_t)B * N * (size_t)((Sq + 31) / 32) * (size_t)block_bank_nka(Skv, by) * 2048);
 }
 
 static int block_common(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* workspace,
@@ -506,12 +511,12 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
   } else {
     a.max_chunks = 1;
   }
-  // A workspace large enough for the dS bank (block sizes multiples of 32) selects the dQ
-  // path that reads the dS blocks the dK/dV kernel stores instead of recomputing S and dP.
+  // A workspace large enough for the dS bank selects the dQ path that reads the dS blocks the
+  // dK/dV kernel stores instead of recomputing S and dP.
   if (block_bank_ok(Sq, Skv, bx, by) &&
       workspace_bytes >= blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, D, bx, by)) {
     a.ds_bank = at<uint16_t>(workspace, L.total);
-    a.ds_nka = (Skv + 31) / 32;
+    a.ds_nka = (int)block_bank_nka(Skv, by);
     a.ds_blocks = (long long)((Sq + 31) / 32) * a.ds_nka;
   }
   e = ma::launch_block_bwd(dtype, a, hs, events ? (hipEvent_t)events[2] : nullptr);

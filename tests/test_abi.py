@@ -167,9 +167,10 @@ def test_ds_workspace_head_split(lib):
 
 
 def test_block_ds_workspace_query(lib):
-    """The block path's dS-bank workspace: the minimum one plus 2048 bytes per cell of the
-    dense grid of 32 x 32 blocks of every (batch, query head) when bx and by are multiples of
-    32; the minimum one otherwise (no bank: the tilings of the two kernels differ)."""
+    """The block path's dS-bank workspace: the minimum one plus 2048 bytes per cell of a
+    grid of 32 x 32 blocks of every (batch, query head): 32-row query halves by the dense
+    32-row key grid when by is a multiple of 32, else by ceil(by / 32) sub-blocks per mask
+    block (the dK/dV workgroup's key tiling, which starts at every block's first row)."""
     Z, I = ctypes.c_size_t, ctypes.c_int
     lib.blocksparse_attn_bwd_workspace_bytes.restype = Z
     lib.blocksparse_attn_bwd_workspace_bytes.argtypes = [I] * 7
@@ -180,11 +181,9 @@ def test_block_ds_workspace_query(lib):
         base = lib.blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, 128, bx, by)
         full = lib.blocksparse_attn_bwd_ds_workspace_bytes(B, N, Sq, Skv, 128, bx, by)
         assert base > 0
-        if bx % 32 == 0 and by % 32 == 0:
-            bank = B * N * (-(-Sq // 32)) * (-(-Skv // 32)) * 2048
-            assert full == base + (bank + 255) // 256 * 256, (B, N, Sq, Skv, bx, by)
-        else:
-            assert full == base, (bx, by)
+        nka = -(-Skv // 32) if by % 32 == 0 else -(-Skv // by) * -(-by // 32)
+        bank = B * N * (-(-Sq // 32)) * nka * 2048
+        assert full == base + (bank + 255) // 256 * 256, (B, N, Sq, Skv, bx, by)
     assert lib.blocksparse_attn_bwd_ds_workspace_bytes(1, 16, 8192, 8192, 128, 64, 64) == \
         lib.blocksparse_attn_bwd_workspace_bytes(1, 16, 8192, 8192, 128, 64, 64) + 16 * 256 * 256 * 2048
     assert lib.blocksparse_attn_bwd_ds_workspace_bytes(1, 4, 128, 128, 64, 64, 64) == 0   # D = 64

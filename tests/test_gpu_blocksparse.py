@@ -27,8 +27,8 @@ def with_oracle_forward(wl, x):
 
 
 def gpu_bwd(wl, x, path="default"):
-    """path "default": the binding's workspace (the dS bank when bx and by are multiples of 32);
-    "recompute": the minimum workspace (dQ recomputes S and dP)."""
+    """path "default": the binding's workspace (the dS bank); "recompute": the minimum
+    workspace (dQ recomputes S and dP)."""
     g = {k: v.to(DEV) for k, v in x.items()}
     print(f"[gpu] blocksparse_attn_bwd {wl.name} B{wl.B} N{wl.Hq} Sq{wl.Sq} Skv{wl.Skv} bx{wl.bx} by{wl.by} {path}",
           flush=True)
@@ -44,7 +44,7 @@ def gpu_bwd(wl, x, path="default"):
 
 
 def banked(wl):
-    return wl.bx % 32 == 0 and wl.by % 32 == 0
+    return wl.bx % 16 == 0 and wl.by % 16 == 0
 
 
 @pytest.mark.parametrize("name", ["bigbird", "ragged"])
@@ -95,10 +95,19 @@ SMALL = [
     W.custom_blocksparse("b16x64_dense_3chunks_bf16", 1, 1, 1100, 200, 16, 64, "dense", dtype=torch.bfloat16,
                          seed_base=213),
     W.custom_blocksparse("b64_bigbird_chunked", 1, 1, 2300, 2300, 64, 64, "bigbird", seed_base=214),
+    # bx = 48: two selected query blocks can share a 32-row query half (one dS bank entry), and a
+    # chunk boundary between them moves past the second.  Random: 63 query blocks at density
+    # 0.7, two chunks per key block with boundaries at random entries; GQA dense: 21 query
+    # blocks per head, so the boundary at entry 32 falls on the second head's block 11, which
+    # shares a half with its block 10.
+    W.custom_blocksparse("b48x64_random_chunked", 1, 2, 3000, 700, 48, 64, "random", density=0.7,
+                         seed_base=215),
+    W.custom_blocksparse("b48x80_dense_gqa_chunked_bf16", 1, 2, 1000, 400, 48, 80, "dense", dtype=torch.bfloat16,
+                         seed_base=216, Nkv=1),
 ]
 
 
-# Block sizes that are multiples of 32 run both dQ paths (dS bank, recompute); others have one.
+# Every block size runs both dQ paths (dS bank, recompute).
 SMALL_PATHS = [(wl, p) for wl in SMALL for p in (("default", "recompute") if banked(wl) else ("default",))]
 
 
