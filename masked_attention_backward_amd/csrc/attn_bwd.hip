@@ -219,8 +219,10 @@ static void launch_block_t(const AttnArgs& a, hipStream_t st, hipEvent_t ev_mid)
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   if (a.ds_bank && (a.bx % 32 != 0 || a.by % 32 != 0)) {
     // dS bank with query halves or key sub-blocks off the 32-row grid: one wave per 32-row
-    // query half, four per workgroup.
-    hipLaunchKernelGGL(dq_ds_blocku_kernel<T>, dim3(a.B * a.Hq * ((a.Sq + 127) / 128)), dim3(256), 0, st, a);
+    // query half, DQU_WAVES per workgroup.
+    const int per = 32 * DQU_WAVES;
+    hipLaunchKernelGGL(dq_ds_blocku_kernel<T>, dim3(a.B * a.Hq * ((a.Sq + per - 1) / per)), dim3(DQU_WAVES * 64), 0,
+                       st, a);
     return;
   }
   switch (nwq) {

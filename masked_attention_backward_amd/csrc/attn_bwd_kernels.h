@@ -1298,8 +1298,6 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_ds_block_kernel(const AttnArgs 
   dq_ds_block_tile<T, NW>(a, bh / a.Hq, bh % a.Hq, qb, smem);
 }
 
-// Launch of one (element type, mask kind, NW) variant: dK/dV with 2 NW waves (NW key blocks
-// of 32 rows), dQ with NW waves (NW query blocks of 32 rows).
 // Block path with a dS bank when bx or by is not a multiple of 32 (the dK/dV kernel's 32-row
 // query halves then straddle query blocks, and its key sub-blocks c0 + 32 kb are off the
 // 32-row grid).  Every wave owns one 32-row query half qa (rows 32 qa ..) and works alone:
@@ -1307,12 +1305,31 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_ds_block_kernel(const AttnArgs 
 // query blocks its rows fall in, and for each key block the sub-blocks that hold key rows,
 // one GEMM per sub-block from its dS bank entry (qa, kb NK + j).  The entry exists exactly
 // when one of those query blocks selects kb (the dK/dV kernel stored it then), and its rows
-// of query blocks that do not select kb are exact zeros.  Key rows and dS blocks go through
-// the wave's own two LDS buffers (one sub-block ahead, LDS DMA, vmcnt waits only: no
-// barriers), so waves of one workgroup never wait for each other.
-constexpr int DQU_BUF_BYTES = 8192 + 2048;          // 32 key rows, one 32 x 32 dS block
-constexpr int DQU_WAVE_BYTES = 2 * DQU_BUF_BYTES;    // two buffers per wave (20 KiB)
-static_assert(DQU_WAVE_BYTES >= EPI_ELEMS * 2, "the epilogue stages through the wave's buffers");
+// of query blocks that do not select kb are exact zeros.
+// The walk is latency-bound (a few dozen dependent sub-blocks per wave, little arithmetic
+// each), so the copies go in granules of 16 keys, one MFMA k-step: 4 KiB of K rows and the
+// 1 KiB of the dS entry those keys need, through a ring of DQU_SLOTS granule slots private to
+// the wave (LDS DMA, vmcnt waits only: no barriers), DQU_SLOTS - 1 granules in flight.
+// In a slot, K rows sit at 0 .. 4 KiB with the swizzle of a staged tile's first 16 rows (the
+// swizzle repeats every 16 rows, so the k-step's fragments read as k-step 0), and the dS
+// granule at 4 KiB: the 512 bytes of k-step tt of the entry's unit 0, then those of unit 1.
+constexpr int DQU_SLOT_BYTES = 4096 + 1024;
+constexpr int DQU_SLOTS = 5;
+constexpr int DQU_WAVE_BYTES = DQU_SLOTS * DQU_SLOT_BYTES;   // 25 KiB per wave
+constexpr int DQU_WAVES = 2;                                 // waves (query halves) per workgroup
+static_assert(DQU_WAVE_BYTES >= EPI_ELEMS * 2, "the epilogue stages through the wave's slots");
+
+// vmcnt wait for a count known only at run time (multiples of five, the copies per granule).
+__device__ __forceinline__ void wait_vmcnt_granules(int pending) {
+  static_assert(DQU_SLOTS == 5, "one case per granule count");
+  switch (pending) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<5>(); break;
+    case 2: wait_vmcnt<10>(); break;
+    case 3: wait_vmcnt<15>(); break;
+    default: wait_vmcnt<20>(); break;
+  }
+}
 
 template <class T>
 __device__ __forceinline__ void dq_ds_blocku_wave(const AttnArgs& a, int b, int hq, int qa, uint16_t* buf,
@@ -1353,41 +1370,51 @@ __device__ __forceinline__ void dq_ds_blocku_wave(const AttnArgs& a, int b, int 
       if (pos[i] < cnt[i] && sel[i][pos[i]] == m) ++pos[i];
     return m;
   };
-  // The sub-block after (kb, j): the next one of kb that holds key rows, else the next key block.
-  auto advance = [&](int& kb, int& j) {
-    ++j;
-    if (j >= nks || kb * a.by + 32 * j >= min(kb * a.by + a.by, skv)) {
-      kb = next_kb();
-      j = 0;
-    }
-  };
 
-  auto src_chunk = [&](int u) -> uint32_t {
-    const int m = 2 * (lane >> 4) + (((lane >> 3) & 1) ^ u);
-    return (uint32_t)(u * 1024 + (32 * ((lane >> 2) & 1) + 4 * m + (lane & 3)) * 16);
+  // dS copy sources: the lane filling byte 16 l of a slot's dS granule (unit l / 32, k-step tt)
+  // fetches the entry's 16-byte chunk that the sub-block layout places at slot 32 tt + l % 32
+  // of that unit.
+  auto ds_src = [&](int tt) -> uint32_t {
+    const int u = lane >> 5, P = 32 * tt + (lane & 31);
+    const int m = 2 * (P >> 4) + (((P >> 3) & 1) ^ u);
+    return (uint32_t)(u * 1024 + (32 * ((P >> 2) & 1) + 4 * m + (P & 3)) * 16);
   };
-  const uint32_t so0 = src_chunk(0), so1 = src_chunk(1);
+  const uint32_t dsrc0 = ds_src(0), dsrc1 = ds_src(1);
   const int g = (lane >> 4) & 1, ia = lane & 3, ir = (lane >> 2) & 3;
-  const int dso = g * 1024 + 128 * (g ^ h) + 64 * (ia & 1) + 16 * ir + 8 * (ia >> 1);
-  // Key rows of a sub-block: unit u (four rows) per instruction, row 4 u + lane / 16 of the 32,
-  // the swizzle of a staged tile's first 32 rows, rows past the end clamped (their dS is 0).
-  uint32_t kcol[8];
+  const int dso = 4096 + g * 512 + 128 * (g ^ h) + 64 * (ia & 1) + 16 * ir + 8 * (ia >> 1);
+  // Key rows of a granule: unit u (four rows) per instruction, row 4 u + lane / 16 of the 16.
+  uint32_t kcol[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 4; ++u) {
     const int row = 4 * u + (lane >> 4);
     kcol[u] = (uint32_t)((((lane & 15) ^ swz(row)) << 3));
   }
-  auto issue = [&](int kb, int j, int s) {
-    const int row0 = kb * a.by + 32 * j;
-    const uint32_t d = buf_lds + (uint32_t)(s * DQU_BUF_BYTES);
+  // Granule cursor: key block kb, sub-block j, k-step tt (kb < 0: no granule left).
+  int kb = next_kb(), j = 0, tt = 0;
+  auto issue = [&](int slot) {
+    const int row0 = kb * a.by + 32 * j + 16 * tt;
+    const uint32_t d = buf_lds + (uint32_t)(slot * DQU_SLOT_BYTES);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int gr = min(row0 + 4 * u + (lane >> 4), skv - 1);
       dma16(Kp, 2u * ((uint32_t)gr * HD + kcol[u]), __builtin_amdgcn_readfirstlane(d + (uint32_t)(u * 1024)));
     }
     const uint16_t* blk = bank + (long long)(kb * nks + j) * 1024;
-    dma16nt(blk, so0, __builtin_amdgcn_readfirstlane(d + 8192u));
-    dma16nt(blk, so1, __builtin_amdgcn_readfirstlane(d + 9216u));
+    dma16nt(blk, tt ? dsrc1 : dsrc0, __builtin_amdgcn_readfirstlane(d + 4096u));
+    // Advance: the entry's second k-step if it holds key rows of the block (its dS columns are
+    // zeros otherwise), else the next sub-block holding key rows, else the next key block of
+    // the union.
+    const int kend = min(kb * a.by + a.by, skv);
+    if (tt == 0 && row0 + 16 < kend) {
+      tt = 1;
+    } else {
+      tt = 0;
+      ++j;
+      if (j >= nks || kb * a.by + 32 * j >= kend) {
+        kb = next_kb();
+        j = 0;
+      }
+    }
   };
 
   f32x16 acc[4];
@@ -1396,54 +1423,52 @@ __device__ __forceinline__ void dq_ds_blocku_wave(const AttnArgs& a, int b, int 
   FragOff fo(lane);
   typedef short short4v __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) short4v* lds_ptr;
-  auto ds_frag = [&](const char* blk, int tt) -> u32x4 {
-    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt));
-    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(blk + dso + 512 * tt + 256));
-    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
-    return (u32x4){xa[0], xa[1], ya[0], ya[1]};
-  };
 
-  int kb = next_kb(), j = 0, s = 0;
-  if (kb >= 0) issue(kb, j, 0);
-  while (kb >= 0) {
-    int nk = kb, nj = j;
-    advance(nk, nj);
-    if (nk >= 0) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the other buffer done
-      issue(nk, nj, s ^ 1);
-      wait_vmcnt<10>();   // this sub-block's ten copies landed; the next one's may fly
-    } else {
-      wait_vmcnt<0>();
-    }
-    const uint16_t* kt = buf + s * (DQU_BUF_BYTES / 2);
-    const char* dsb = reinterpret_cast<const char*>(buf) + s * DQU_BUF_BYTES + 8192;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const u32x4 fa = ds_frag(dsb, tt);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa, frag_col(kt, fo, 0, tt, nb), acc[nb]);
-    }
-    kb = nk;
-    j = nj;
-    s ^= 1;
+  int inflight = 0, slot_in = 0, slot_out = 0;
+  while (inflight < DQU_SLOTS - 1 && kb >= 0) {
+    issue(slot_in);
+    slot_in = slot_in == DQU_SLOTS - 1 ? 0 : slot_in + 1;
+    ++inflight;
   }
-  // Epilogue through the wave's own buffers (every copy landed, every read done).
+  while (inflight > 0) {
+    if (kb >= 0) {
+      // The slot refilled held the granule computed last: its LDS reads are done first.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(slot_in);
+      slot_in = slot_in == DQU_SLOTS - 1 ? 0 : slot_in + 1;
+      ++inflight;
+    }
+    wait_vmcnt_granules(inflight - 1);   // the oldest granule landed; the younger ones may fly
+    const char* sb = reinterpret_cast<const char*>(buf) + slot_out * DQU_SLOT_BYTES;
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(sb + dso));
+    const short4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(sb + dso + 256));
+    const u32x2 xa = __builtin_bit_cast(u32x2, x), ya = __builtin_bit_cast(u32x2, y);
+    const u32x4 fa = (u32x4){xa[0], xa[1], ya[0], ya[1]};
+    const uint16_t* kt = reinterpret_cast<const uint16_t*>(sb);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(fa, frag_col(kt, fo, 0, 0, nb), acc[nb]);
+    slot_out = slot_out == DQU_SLOTS - 1 ? 0 : slot_out + 1;
+    --inflight;
+  }
+  // Epilogue through the wave's own slots (every copy landed, every read done).
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   store_tile_rows<T>(acc, a.scale, (uint16_t*)a.dq + (qrow0 + q0) * HD, min(32, sq - q0), buf, lane);
 }
 
 template <class T>
-__global__ __launch_bounds__(4 * 64, 2) void dq_ds_blocku_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * DQU_WAVE_BYTES / 2];
+__global__ __launch_bounds__(DQU_WAVES * 64) void dq_ds_blocku_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[DQU_WAVES * DQU_WAVE_BYTES / 2];
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  // Four 32-row halves per workgroup.  Workgroups of one (batch, head) are consecutive modulo
-  // B Hq, so with B Hq a multiple of 8 each lands on the XCD that holds its head's K rows and
-  // bank blocks in L2.
+  // DQU_WAVES 32-row halves per workgroup.  Workgroups of one (batch, head) are consecutive
+  // modulo B Hq, so with B Hq a multiple of 8 each lands on the XCD that holds its head's K
+  // rows and bank blocks in L2.
   const int nbh = a.B * a.Hq;
   const int bh = blockIdx.x % nbh, t = blockIdx.x / nbh;
-  dq_ds_blocku_wave<T>(a, bh / a.Hq, bh % a.Hq, 4 * t + w, smem + w * (DQU_WAVE_BYTES / 2), lane);
+  dq_ds_blocku_wave<T>(a, bh / a.Hq, bh % a.Hq, DQU_WAVES * t + w, smem + w * (DQU_WAVE_BYTES / 2), lane);
 }
 
+// Launch of one (element type, mask kind, NW) variant: dK/dV with 2 NW waves (NW key blocks
+// of 32 rows), dQ with NW waves (NW query blocks of 32 rows).
 template <class T, int MASK, int NW>
 inline void launch_dkdv_only(const AttnArgs& a, int grid, hipStream_t st) {
   if (a.ds_bank) {
