@@ -54,8 +54,7 @@ BOUND = {"tiny": "launch", "mid": "hbm", "large_w128": "hbm", "large_causal": "m
          "ragged": "mfma", "pages_h64_s4096": "mfma", "pages_h64_s4096_fwd": "mfma", "varlen_8x2048": "mfma",
          "varlen_mixed": "mfma"}
 # Workspace size that selects the dQ path ("ds_bank": the dK/dV kernel stores dS and dQ is one
-# GEMM per block -- on the block path only when bx and by are multiples of 32, the library
-# recomputing otherwise; "recompute": the minimum workspace, dQ recomputes S and dP).
+# GEMM per block; "recompute": the minimum workspace, dQ recomputes S and dP).
 DQ_PATH = "ds_bank"
 CONFIG_ORDER = ["tiny", "mid", "large_w128", "large_causal", "bigbird", "ragged", "pages_h64_s4096",
                 "pages_h64_s4096_fwd", "varlen_8x2048", "varlen_mixed"]
@@ -312,10 +311,8 @@ class Case:
 
 def dq_path_of(case):
     """The dQ path a backward case runs (None for the forward)."""
-    if case.kind in ("sink", "varlen"):
+    if case.kind in ("sink", "varlen", "blocksparse"):
         return DQ_PATH
-    if case.kind == "blocksparse":
-        return DQ_PATH if case.wl.bx % 32 == 0 and case.wl.by % 32 == 0 else "recompute"
     return None
 
 

@@ -355,8 +355,8 @@ def blocksparse_attn_bwd(q, k, v, o, do, lse, block_mask, bx, by, scale=None, wo
     """Block-sparse backward -> (dq, dk, dv); k/v (and dk/dv) may have fewer heads (GQA).
 
     Without a workspace one of blocksparse_attn_bwd_ds_workspace_bytes() is allocated (the
-    dS-bank path when bx and by are multiples of 32), or of the minimum size when the bank would
-    take more than half of the free device memory; a caller workspace of
+    dS-bank path), or of the minimum size when the bank would take more than half of the free
+    device memory; a caller workspace of
     blocksparse_attn_bwd_workspace_bytes() selects the recompute path."""
     B, N, Nkv, Sq, Skv, D = _block_shapes(q, k, block_mask, bx, by)
     dev = q.device
