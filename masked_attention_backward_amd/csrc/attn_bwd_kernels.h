@@ -1351,23 +1351,30 @@ __device__ __forceinline__ void dq_ds_blocku_wave(const AttnArgs& a, int b, int 
   const size_t qhead = (size_t)b * a.Hq + hq;
   const int qb0 = q0 / a.bx, qb1 = min(a.nqb - 1, (min(q0 + 32, sq) - 1) / a.bx);
   const_int_ptr sel[3];
-  int cnt[3], pos[3] = {0, 0, 0};
+  int cnt[3], pos[3] = {0, 0, 0}, head[3];
+  constexpr int kDone = 0x7fffffff;
+  // head[i]: entry pos[i] of list i (kDone past its end).  A list's next entry is loaded when
+  // its head is consumed and first used by the following merge, several granules later, so
+  // the scalar loads stay off the wave's path (a row's entries past its count are in bounds:
+  // the table pads every row to nkb entries, and the index is clamped to the row).
+  auto entry = [&](int i) -> int { return pos[i] < cnt[i] ? sel[i][min(pos[i], a.nkb - 1)] : kDone; };
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int qb = min(qb0 + i, qb1);
     sel[i] = (const_int_ptr)a.sel_q + (qhead * a.nqb + qb) * a.nkb;
     cnt[i] = qb0 + i <= qb1 ? ((const_int_ptr)a.cnt_q)[qhead * a.nqb + qb] : 0;
+    head[i] = entry(i);
   }
   // Next key block of the union (ascending; -1 when done).
   auto next_kb = [&]() -> int {
-    int m = 0x7fffffff;
+    const int m = min(head[0], min(head[1], head[2]));
+    if (m == kDone) return -1;
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      if (pos[i] < cnt[i]) m = min(m, sel[i][pos[i]]);
-    if (m == 0x7fffffff) return -1;
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (pos[i] < cnt[i] && sel[i][pos[i]] == m) ++pos[i];
+      if (head[i] == m) {
+        ++pos[i];
+        head[i] = entry(i);
+      }
     return m;
   };
 
