@@ -194,10 +194,11 @@ int blocksparse_attn_fwd(const void* q, const void* k, const void* v, const uint
  *   mask_t [B, N, nkb, nqb] u8,
  *   sel_q [B, N, nqb, nkb] i32, cnt_q [B, N, nqb] i32, sel_k [B, N, nkb, nqb] i32,
  *   cnt_k [B, N, nkb] i32,
- *   when N * nqb > 32: fp32 partial dK and dV of key blocks selected by more than 32 query
+ *   when N * nqb > 64: fp32 partial dK and dV of key blocks selected by more than 32 query
  *   blocks (summed over a GQA group's query heads), which the backward splits over several
  *   workgroups and adds back in a fixed order: 2 x B x floor(N * (nqb + 31) / 32) slots of
- *   [Skvp, D] (Skvp = 64*ceil(Skv/64)), a bound that holds for every Hkv dividing N.
+ *   [Skvp, D] (Skvp = 64*ceil(Skv/64)), a bound that holds for every Hkv dividing N.  A call
+ *   whose group * nqb is at most 64 splits nothing (one workgroup walks each key block).
  * The block-sparse forward calls take the same workspace. */
 size_t blocksparse_attn_bwd_workspace_bytes(int B, int N, int Sq, int Skv, int D, int bx, int by);
 

@@ -54,9 +54,13 @@ int check_blocks(int bx, int by) {
 // workgroups whose fp32 partial sums a reduce kernel adds in a fixed order.
 constexpr int kBlockChunk = 32;
 
-// Chunks per (kv head, key block) the dK/dV grid provides: ceil(group * nqb / kBlockChunk).
+// Chunks per (kv head, key block) the dK/dV grid provides: ceil(group * nqb / kBlockChunk),
+// or 1 when a key block has at most 2 kBlockChunk possible entries (one workgroup then walks at
+// most twice the usual count, which costs less than the partial sums, the reduce kernel and the
+// idle chunk slots of a split that most shapes of this size never use).
 int block_max_chunks(int N, int Nkv, int nqb) {
   const long long g = N / Nkv;
+  if (g * nqb <= 2 * kBlockChunk) return 1;
   return (int)((g * nqb + kBlockChunk - 1) / kBlockChunk);
 }
 
@@ -66,7 +70,7 @@ struct BlockLayout {
 
 // The partial-sum region is sized for any Nkv dividing N: Nkv * ceil((N / Nkv) * nqb / C) <=
 // floor(N * (nqb + C - 1) / C) chunk slots per batch, each of padded Skv rows of D fp32 values,
-// for dK and for dV.  It is absent when no key block can need more than one chunk.
+// for dK and for dV.  It is absent when no key block can be split (N * nqb <= 2 kBlockChunk).
 BlockLayout block_layout(int B, int N, int Sq, int Skv, int nqb, int nkb) {
   BlockLayout l;
   const size_t bn = (size_t)B * N;
@@ -79,7 +83,7 @@ BlockLayout block_layout(int B, int N, int Sq, int Skv, int nqb, int nkb) {
   l.cnt_k = align256(l.sel_k + bn * nkb * nqb * sizeof(int32_t));
   l.part = align256(l.cnt_k + bn * nkb * sizeof(int32_t));
   l.total = l.part;
-  if ((long long)N * nqb > kBlockChunk) {
+  if ((long long)N * nqb > 2 * kBlockChunk) {
     const size_t slots = (size_t)B * (((size_t)N * (nqb + kBlockChunk - 1)) / kBlockChunk);
     l.total = align256(l.part + 2 * slots * pad64(Skv) * ma::HD * sizeof(float));
   }

@@ -88,21 +88,22 @@ SMALL = [
     W.custom_blocksparse("b64_window200_bf16", 1, 2, 450, 450, 64, 64, "window", dtype=torch.bfloat16,
                          seed_base=210, window=200),
     W.custom_blocksparse("b32x16_window100", 2, 1, 333, 333, 32, 16, "window", seed_base=211, window=100),
-    # Key blocks selected by more than 32 query blocks are split over several dK/dV workgroups
-    # (fp32 partials summed in chunk order): two and three chunks, and bigbird's global columns
-    # (two chunks) next to single-chunk key blocks.
-    W.custom_blocksparse("b16x32_dense_2chunks", 1, 2, 700, 300, 16, 32, "dense", seed_base=212),
+    # Shapes whose key blocks can be selected by more than 64 query blocks split them over
+    # several dK/dV workgroups of at most 32 (fp32 partials summed in chunk order): two chunks
+    # (random, about 48 of 69), three (dense), and bigbird's global columns (three chunks) next
+    # to single-chunk key blocks.
+    W.custom_blocksparse("b16x32_random_2chunks", 1, 2, 1100, 300, 16, 32, "random", density=0.7, seed_base=212),
     W.custom_blocksparse("b16x64_dense_3chunks_bf16", 1, 1, 1100, 200, 16, 64, "dense", dtype=torch.bfloat16,
                          seed_base=213),
-    W.custom_blocksparse("b64_bigbird_chunked", 1, 1, 2300, 2300, 64, 64, "bigbird", seed_base=214),
+    W.custom_blocksparse("b64_bigbird_chunked", 1, 1, 4200, 4200, 64, 64, "bigbird", seed_base=214),
     # bx = 48: two selected query blocks can share a 32-row query half (one dS bank entry), and a
-    # chunk boundary between them moves past the second.  Random: 63 query blocks at density
-    # 0.7, two chunks per key block with boundaries at random entries; GQA dense: 21 query
-    # blocks per head, so the boundary at entry 32 falls on the second head's block 11, which
-    # shares a half with its block 10.
-    W.custom_blocksparse("b48x64_random_chunked", 1, 2, 3000, 700, 48, 64, "random", density=0.7,
+    # chunk boundary between them moves past the second.  Random: 67 query blocks at density
+    # 0.7, two chunks per key block with boundaries at random entries; GQA dense: 35 query
+    # blocks per head, so the boundary at entry 64 falls on the second head's block 29, which
+    # shares a half with its block 28.
+    W.custom_blocksparse("b48x64_random_chunked", 1, 2, 3200, 700, 48, 64, "random", density=0.7,
                          seed_base=215),
-    W.custom_blocksparse("b48x80_dense_gqa_chunked_bf16", 1, 2, 1000, 400, 48, 80, "dense", dtype=torch.bfloat16,
+    W.custom_blocksparse("b48x80_dense_gqa_chunked_bf16", 1, 2, 1680, 400, 48, 80, "dense", dtype=torch.bfloat16,
                          seed_base=216, Nkv=1),
 ]
 
@@ -159,8 +160,8 @@ GQA = [
     W.custom_blocksparse("gqa_b48x80_random_6to2_bf16", 2, 6, 250, 230, 48, 80, "random", dtype=torch.bfloat16,
                          density=0.4, seed_base=302, Nkv=2),
     W.custom_blocksparse("gqa_b32x128_causal_8to1", 1, 8, 300, 300, 32, 128, "causal", seed_base=303, Nkv=1),
-    # The group's 4 query heads select key block 0 52 times (two chunks), the last one 4 times.
-    W.custom_blocksparse("gqa_b32_causal_chunked_4to1", 1, 4, 400, 400, 32, 32, "causal", seed_base=304, Nkv=1),
+    # The group's 4 query heads select key block 0 76 times (three chunks), the last one 4 times.
+    W.custom_blocksparse("gqa_b32_causal_chunked_4to1", 1, 4, 600, 600, 32, 32, "causal", seed_base=304, Nkv=1),
 ]
 
 
