@@ -2,6 +2,7 @@
 // the dK/dV and dQ kernels (their templates are in attn_bwd_kernels.h; each variant is
 // instantiated in its own object, see attn_bwd_variant.hip).
 #include "attn_bwd_kernels.h"
+#include "ma_tables.h"
 
 namespace ma {
 
@@ -16,13 +17,11 @@ namespace ma {
 // sequence b at rows cu[b] .. cu[b + 1] (clamped as the attention kernels clamp them); the
 // per-row buffers stay [B, H, padded S] either way.
 template <class T, bool SINK, bool STREAM>
-__global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ dout,
-                                                         const float* __restrict__ lse,
-                                                         const float* __restrict__ sink, float* __restrict__ delta,
-                                                         float* __restrict__ lse2, float* __restrict__ part, int H,
-                                                         int S, int nblk, const int* __restrict__ cu, int total) {
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void preprocess_rows(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                const float* __restrict__ lse, const float* __restrict__ sink,
+                                                float* __restrict__ delta, float* __restrict__ lse2,
+                                                float* __restrict__ part, int H, int S, int nblk,
+                                                const int* __restrict__ cu, int total, int blk, int h, int b) {
   const int tid = threadIdx.x, rsub = tid >> 4, ch = tid & 15;
   __shared__ float sd[64];
   size_t head = ((size_t)b * H + h) * (size_t)S;
@@ -102,6 +101,39 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
   }
 }
 
+template <class T, bool SINK, bool STREAM>
+__global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ sink, float* __restrict__ delta,
+                                                         float* __restrict__ lse2, float* __restrict__ part, int H,
+                                                         int S, int nblk, const int* __restrict__ cu, int total) {
+  preprocess_rows<T, SINK, STREAM>(o, dout, lse, sink, delta, lse2, part, H, S, nblk, cu, total, blockIdx.x,
+                                   blockIdx.y, blockIdx.z);
+}
+
+// Block path: the selection tables and the preprocess are independent, so one launch runs
+// both: blocks [0, ntab) build table rows (head bn = i % BN, row group i / BN), the rest take
+// one 64-row block of Delta / lse2 each; their latencies overlap and a kernel boundary goes.
+template <class T, bool STREAM>
+__global__ __launch_bounds__(256) void block_prep_kernel(const uint8_t* __restrict__ mask, int nqb, int nkb,
+                                                         uint8_t* __restrict__ mask_t, int* __restrict__ sel_q,
+                                                         int* __restrict__ cnt_q, int* __restrict__ sel_k,
+                                                         int* __restrict__ cnt_k, int BN, int ntab,
+                                                         const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         const float* __restrict__ lse, float* __restrict__ delta,
+                                                         float* __restrict__ lse2, int H, int S, int nblk) {
+  const int i = blockIdx.x;
+  if (i < ntab) {
+    mask_table_rows(mask, nqb, nkb, mask_t, sel_q, cnt_q, sel_k, cnt_k, i % BN, i / BN);
+    return;
+  }
+  const int j = i - ntab;
+  const int blk = j % nblk, h = (j / nblk) % H, b = j / (nblk * H);
+  preprocess_rows<T, false, STREAM>(o, dout, lse, nullptr, delta, lse2, nullptr, H, S, nblk, nullptr, 0, blk, h, b);
+}
+
 // Key blocks (block path) or key tiles (window path, head split) whose dK/dV sums span several
 // workgroups: sum the fp32 partials in chunk order (fixed, so results are bit-identical run to
 // run) and cast.  A 256-thread block covers 8 key rows x 128 columns (4 columns per thread) of
@@ -148,6 +180,30 @@ static hipError_t launch_preprocess_t(const void* o, const void* dout, const flo
   } else {
     if (stream) go(preprocess_kernel<T, false, true>);
     else go(preprocess_kernel<T, false, false>);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_prep(int dtype, const uint8_t* mask, int B, int N, int nqb, int nkb, uint8_t* mask_t,
+                             int* sel_q, int* cnt_q, int* sel_k, int* cnt_k, const void* o, const void* dout,
+                             const float* lse, float* delta, float* lse2, int S, hipStream_t st) {
+  const int BN = B * N, rows = nqb > nkb ? nqb : nkb;
+  const int ntab = BN * ((rows + 3) / 4);
+  const int nblk = (S + 63) / 64;
+  const long long nblocks = (long long)ntab + (long long)nblk * N * B;
+  if (nblocks > 0x7fffffffll) return hipErrorInvalidValue;
+  const bool stream = (long long)B * N * S * HD * 2 * 2 > (192ll << 20);   // as launch_preprocess_t
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(256), 0, st, mask, nqb, nkb, mask_t, sel_q, cnt_q,
+                       sel_k, cnt_k, BN, ntab, (const uint16_t*)o, (const uint16_t*)dout, lse, delta, lse2, N, S,
+                       nblk);
+  };
+  if (dtype == 1) {
+    if (stream) go(block_prep_kernel<BF16, true>);
+    else go(block_prep_kernel<BF16, false>);
+  } else {
+    if (stream) go(block_prep_kernel<F16, true>);
+    else go(block_prep_kernel<F16, false>);
   }
   return hipGetLastError();
 }

@@ -482,13 +482,12 @@ static int block_bwd_impl(const void* q, const void* k, const void* v, const voi
   const BlockLayout L = block_layout(B, N, Sq, Skv, nqb, nkb);
   hipStream_t hs = (hipStream_t)stream;
   if (events) hipEventRecord((hipEvent_t)events[0], hs);
-  hipError_t e = ma::launch_mask_tables(block_mask, B * N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
-                                        at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
-                                        at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), hs);
-  if (e != hipSuccess) return MA_ELAUNCH;
   float* delta = at<float>(workspace, L.delta);
   float* lse2 = at<float>(workspace, L.lse2);
-  e = ma::launch_preprocess(dtype, o, dout, lse, nullptr, delta, lse2, nullptr, B, N, Sq, hs);
+  hipError_t e = ma::launch_block_prep(dtype, block_mask, B, N, nqb, nkb, at<uint8_t>(workspace, L.mask_t),
+                                       at<int>(workspace, L.sel_q), at<int>(workspace, L.cnt_q),
+                                       at<int>(workspace, L.sel_k), at<int>(workspace, L.cnt_k), o, dout, lse,
+                                       delta, lse2, Sq, hs);
   if (e != hipSuccess) return MA_ELAUNCH;
   if (events) hipEventRecord((hipEvent_t)events[1], hs);
   AttnArgs a = base_args(q, k, v, B, N, Nkv, Sq, Skv, scale);
