@@ -93,6 +93,23 @@ def test_workspace_queries(lib):
     assert lib.blocksparse_attn_bwd_workspace_bytes(2, 8, 3000, 3000, 128, 48, 144) == 0   # by > 128
 
 
+def test_block_partial_region_threshold(lib):
+    """The block path splits a key block over several dK/dV workgroups only when N * nqb > 64
+    (a key block can have more than two chunks' worth of entries); the fp32 partial region
+    (2 x B x floor(N (nqb + 31) / 32) slots of padded Skv x 128) exists exactly then."""
+    Z, I = ctypes.c_size_t, ctypes.c_int
+    lib.blocksparse_attn_bwd_workspace_bytes.restype = Z
+    lib.blocksparse_attn_bwd_workspace_bytes.argtypes = [I] * 7
+    ws = lambda B, N, Sq, Skv: lib.blocksparse_attn_bwd_workspace_bytes(B, N, Sq, Skv, 128, 32, 64)
+    for B, N, nqb_lo in [(1, 1, 64), (2, 2, 32), (1, 4, 16)]:
+        Skv = 300
+        lo, hi = ws(B, N, 32 * nqb_lo, Skv), ws(B, N, 32 * nqb_lo + 32, Skv)   # N * nqb = 64 vs 64 + N
+        nqb = nqb_lo + 1
+        region = 2 * B * ((N * (nqb + 31)) // 32) * 320 * 128 * 4
+        tables = B * N * (4 * 32 * nqb_lo + 4 * 32 * nqb_lo)   # generous bound on the other growth
+        assert region <= hi - lo <= region + tables + 8 * 256, (B, N, lo, hi, region)
+
+
 def brute_band_blocks(S, W):
     """32 x 32 (query block, key block) pairs of one head holding a visible (i, j), 0 <= i - j < W."""
     n = (S + 31) // 32
